@@ -1,0 +1,9 @@
+"""MI355X (gfx950) exact attention: tiled forward with online softmax and LSE,
+and the recompute-from-LSE backward, behind a C ABI (include/fa.h).
+
+The Python layer only marshals arguments to libfa_mi355x.so; see binding.py.
+"""
+
+from .binding import (  # noqa: F401
+    FA_DTYPE_BF16, FA_DTYPE_F32, FaError, backward, forward, load_library, workspace_size,
+)

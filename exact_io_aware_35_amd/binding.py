@@ -1,0 +1,151 @@
+"""Thin ctypes binding over the C ABI in include/fa.h (libfa_mi355x.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind fa_forward / fa_backward. PyTorch supplies device memory and
+the current stream. If the shared library is missing the calls raise; there
+is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F32 = 1
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE = 3
+FA_ERR_HIP = 4
+
+# (name, restype, argtypes) of every entry point the header declares.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+SIGNATURES = [
+    ("fa_forward", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
+    ("fa_backward_workspace_size", _SZ, [_I, _I, _I, _I, _I]),
+    ("fa_backward", _I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I,
+                         _I, _P, _SZ, _P]),
+    ("fa_status_string", ctypes.c_char_p, [_I]),
+    ("fa_last_error_message", ctypes.c_char_p, []),
+]
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load libfa_mi355x.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FaError(-1, f"{p} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(p)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status):
+    if status != FA_OK:
+        msg = lib.fa_last_error_message().decode() or lib.fa_status_string(status).decode()
+        raise FaError(status, msg)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise FaError(FA_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported")
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise FaError(FA_ERR_INVALID_ARG, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise FaError(FA_ERR_INVALID_ARG, f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def forward(q, k, v, causal=False, window=(-1, -1), softmax_scale=None, seqlens_k=None,
+            out=None, lse=None, stream=None):
+    """O, LSE = exact attention of q, k, v ([batch, seqlen, heads, headdim]).
+
+    softmax_scale defaults to 1/sqrt(headdim). seqlens_k: int32 [batch] key
+    lengths on the device, or None. Returns (out, lse) with lse [B, H, N] fp32.
+    """
+    import torch
+    lib = load_library()
+    B, N, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise FaError(FA_ERR_INVALID_ARG, "q, k, v must have the same shape")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.fa_forward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                        _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                        _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale, int(bool(causal)),
+                        int(window[0]), int(window[1]), _dtype_code(q),
+                        _stream_handle(stream, q.device))
+    _check(lib, st)
+    return out, lse
+
+
+def workspace_size(batch, heads, seqlen, headdim, dtype_code=FA_DTYPE_BF16):
+    return int(load_library().fa_backward_workspace_size(batch, heads, seqlen, headdim, dtype_code))
+
+
+def backward(q, k, v, out, lse, dout, causal=False, window=(-1, -1), softmax_scale=None,
+             seqlens_k=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of exact attention, recomputing P from the forward's LSE."""
+    import torch
+    lib = load_library()
+    B, N, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    code = _dtype_code(q)
+    need = int(lib.fa_backward_workspace_size(B, H, N, D, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.fa_backward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                         _dev_ptr(out, "out"), _dev_ptr(lse, "lse"), _dev_ptr(dout, "dout"),
+                         _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
+                         _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale,
+                         int(bool(causal)), int(window[0]), int(window[1]), code,
+                         _dev_ptr(workspace, "workspace"), workspace.numel(),
+                         _stream_handle(stream, q.device))
+    _check(lib, st)
+    return dq, dk, dv

@@ -1,0 +1,113 @@
+// fa_common.h -- types, launch parameters and small device helpers shared by
+// the forward and backward kernels of the gfx950 attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_params.h"
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+__device__ __forceinline__ int key_len(const MaskParams& m, int b, int N) {
+  if (m.seqlens_k == nullptr) return N;
+  int L = m.seqlens_k[b];
+  return L < 0 ? 0 : (L > N ? N : L);
+}
+
+// Keys visible to at least one query in [qa, qb] (inclusive): [lo, hi).
+__device__ __forceinline__ void key_range(const MaskParams& m, int kl, int qa, int qb,
+                                          int& lo, int& hi) {
+  lo = 0;
+  hi = kl;
+  if (m.wl >= 0) lo = max(0, qa - m.wl);
+  if (m.wr >= 0) hi = min(hi, qb + m.wr + 1);
+  if (hi < lo) hi = lo;
+}
+
+// Every (i, j) with i in [qa, qb], j in [ka, kb] visible?
+__device__ __forceinline__ bool block_all_visible(const MaskParams& m, int kl, int qa, int qb,
+                                                  int ka, int kb) {
+  if (kb >= kl) return false;
+  if (m.wl >= 0 && ka < qb - m.wl) return false;
+  if (m.wr >= 0 && kb > qa + m.wr) return false;
+  return true;
+}
+
+__device__ __forceinline__ bool visible(const MaskParams& m, int kl, int i, int j) {
+  return j < kl && (m.wl < 0 || j >= i - m.wl) && (m.wr < 0 || j <= i + m.wr);
+}
+
+// Work-group id -> (bh, block). Workgroups are dispatched round-robin over the
+// 8 XCDs (hardware id i runs on XCD i % 8), each XCD with its own L2. When the
+// (b, h) count divides by 8, every XCD gets whole (b, h) groups so their K/V
+// stay in one L2; within an XCD the blocks are interleaved over its heads and,
+// for longest-first, ordered by decreasing block index (more keys under a
+// causal mask).
+__device__ __forceinline__ void map_block(int nbh, int nblk, int xcd_groups, int longest_first,
+                                          int& bh, int& blk) {
+  const int i = blockIdx.x;
+  int rank;
+  if (xcd_groups > 0) {
+    const int hpx = nbh / 8;           // (b, h) per XCD
+    const int xcd = i % 8, slot = i / 8;
+    bh = xcd * hpx + slot % hpx;
+    rank = slot / hpx;
+  } else {
+    bh = i % nbh;
+    rank = i / nbh;
+  }
+  blk = longest_first ? (nblk - 1 - rank) : rank;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return log2f(x); }
+
+// Max over the two 32-lane halves: permlane32_swap(x, x) yields the lower
+// half's value in the first result and the upper half's in the second, in
+// every lane.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round-to-nearest-even float -> bf16 bits, two at a time (gfx950 converts in
+// hardware; the conversion is RNE with NaN preserved).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+  f16x2_t v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) { return *reinterpret_cast<const T*>(p); }
+
+}  // namespace fa

@@ -1,0 +1,19 @@
+// fa_launch.h -- host-side launchers behind the C ABI (internal, C++ linkage).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "fa_params.h"
+
+namespace fa {
+
+// Rows of the query block one forward work-group owns.
+int fwd_block_rows(int dtype_is_f32);
+// Enqueue the forward on `stream`; p.nqb must equal ceil(N / fwd_block_rows()).
+hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream);
+
+// Backward: row statistic, then dK/dV (one pass over the queries per key
+// block) and dQ (one pass over the keys per query block).
+hipError_t launch_backward(BwdParams p, int headdim, int dtype_is_f32, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,51 @@
+// fa_params.h -- plain launch-parameter structs shared by the host API and
+// the kernels (no device code, so host-only sources can include it).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Mask description shared by all kernels. Visible(i, j) holds when
+//   j < key_len(b) && (wl < 0 || j >= i - wl) && (wr < 0 || j <= i + wr);
+// a causal mask is folded into wr = 0 by the host.
+struct MaskParams {
+  const int32_t* seqlens_k;  // [B] or null
+  int wl, wr;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  MaskParams mask;
+  int B, H, N;
+  int nqb;               // query blocks per (b, h)
+  float scale_log2;      // softmax_scale * log2(e)
+  int xcd_groups;        // >0: (b,h) count divisible by 8, remap for XCD locality
+  int longest_first;     // 1: dispatch the query blocks with most keys first
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* drow;           // workspace: D_i = sum_d dO_id O_id, [B][H][N] fp32
+  MaskParams mask;
+  int B, H, N;
+  int nblk;              // blocks per (b, h) along the dimension a kernel tiles
+  float scale;           // softmax_scale
+  float scale_log2;      // softmax_scale * log2(e)
+  int xcd_groups;
+};
+
+}  // namespace fa

@@ -1,0 +1,141 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa_mi355x.so).
+ *
+ * The library computes exact attention in the tiled, IO-aware way the
+ * FlashAttention pages describe: K/V tiles are streamed through on-chip memory
+ * under an online softmax (running row max m, running sum l, rescaled partial
+ * O), so the N x N score matrix never reaches HBM; the forward also writes the
+ * per-row log-sum-exp, and the backward rebuilds the probabilities from it.
+ *
+ * Pages cited (title or address, and section):
+ *   [interview] meko1 LLM interview guide, "FlashAttention 深入": sections
+ *               "Online Softmax（增量式 softmax）" and "反向传播：用重计算换显存".
+ *   [scratch]   l189.com/news/1255901 (implementing Flash Attention from scratch
+ *               in PyTorch): §2.2 online softmax, §3.1 blocked forward and the
+ *               LSE statistic, §3.3 backward (recompute P from LSE; softmax
+ *               Jacobian), §5.2 numerical stability, §5.3 causal mask.
+ *   [notes]     claire-chang.com/post/flashattention-introduction, section
+ *               "flash_attn 的程式碼怎麼寫？" (flash_attn_qkvpacked_func docstring):
+ *               (batch, seqlen, nheads, headdim) layout, softmax_scale default
+ *               1/sqrt(headdim), causal flag, window_size (left, right) with
+ *               keys [i - left, i + right] inclusive and -1 meaning unbounded,
+ *               deterministic backward.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous arrays, 16-byte
+ *     aligned. Q, K, V, O, dO, dQ, dK, dV have layout [batch][seqlen][heads]
+ *     [headdim] ([notes]); LSE and the backward's row statistic have layout
+ *     [batch][heads][seqlen], fp32.
+ *   - dtype selects the element type of Q, K, V, O, dO, dQ, dK, dV:
+ *     FA_DTYPE_BF16 (bfloat16; MFMA with fp32 accumulation) or FA_DTYPE_F32.
+ *     LSE is always fp32 (natural log). Outputs are rounded to nearest even.
+ *   - Ownership: the caller owns every buffer, the workspace included. The
+ *     library allocates and frees nothing and keeps no pointer after a call.
+ *   - Asynchrony: work is enqueued on `stream` and the call returns without
+ *     synchronising. A null stream is the default stream.
+ *   - Errors: every argument is checked before any launch. On a check failure
+ *     the call returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED /
+ *     FA_ERR_WORKSPACE and writes nothing; fa_last_error_message() then names
+ *     the argument. If a launch fails, the call returns FA_ERR_HIP and the
+ *     outputs are undefined.
+ *   - Masks: visible(i, j) = (!causal || j <= i)
+ *                         && (window_left  < 0 || j >= i - window_left)
+ *                         && (window_right < 0 || j <= i + window_right)
+ *                         && j < L_b
+ *     where L_b = seqlens_k[b] clamped to [0, seqlen] if seqlens_k is not NULL,
+ *     else seqlen. A query row with no visible key gets O = 0, LSE = -inf and
+ *     zero gradient contributions.
+ *   - Supported sizes: headdim in {64, 128}; batch, heads, seqlen >= 1;
+ *     batch * heads * seqlen < 2^31 and seqlen <= 2^24; softmax_scale finite
+ *     and > 0.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, bad window or scale */
+  FA_ERR_UNSUPPORTED = 2,  /* well-formed but not built: headdim, dtype */
+  FA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  FA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} fa_status_t;
+
+/*
+ * fa_forward -- exact attention forward.
+ * Computes O = softmax(softmax_scale * Q K^T + mask) V and, per query row,
+ * LSE = ln sum_j exp(softmax_scale * q_i . k_j) over visible keys
+ * ([scratch] §3.1 and §2.2; [interview] "Online Softmax").
+ *   q, k, v   in : [batch][seqlen][heads][headdim], dtype
+ *   out       out: [batch][seqlen][heads][headdim], dtype
+ *   lse       out: [batch][heads][seqlen], fp32, natural log (-inf for empty rows)
+ *   seqlens_k in : [batch] int32 key lengths (device), or NULL for "all seqlen"
+ *   softmax_scale : scale of Q K^T; pass 1/sqrt(headdim) for the usual default
+ *   causal        : nonzero keeps keys j <= i ([scratch] §5.3)
+ *   window_left, window_right : sliding window, -1 = unbounded ([notes])
+ * out and lse must not overlap the inputs.
+ */
+fa_status_t fa_forward(const void* q, const void* k, const void* v,
+                       void* out, float* lse, const int32_t* seqlens_k,
+                       int batch, int heads, int seqlen, int headdim,
+                       float softmax_scale, int causal,
+                       int window_left, int window_right,
+                       fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_backward_workspace_size -- bytes of device workspace fa_backward needs
+ * for these sizes (the fp32 row statistic D_i = sum_d dO_id O_id, [batch]
+ * [heads][seqlen], rounded up to 256 bytes). Returns 0 for invalid sizes.
+ */
+size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
+                                  fa_dtype_t dtype);
+
+/*
+ * fa_backward -- gradients of exact attention, recomputing P from the saved
+ * LSE instead of storing it ([interview] "反向传播：用重计算换显存";
+ * [scratch] §3.3):
+ *   P = exp(softmax_scale * Q K^T - LSE) on visible pairs, 0 elsewhere
+ *   dV = P^T dO;  dP = dO V^T;  D_i = sum_d dO_id O_id (= sum_j P_ij dP_ij)
+ *   dS = P * (dP - D);  dQ = softmax_scale * dS K;  dK = softmax_scale * dS^T Q
+ * The softmax Jacobian's row sum is taken over the whole row.
+ *   q, k, v, out, dout  in : [batch][seqlen][heads][headdim], dtype; out is
+ *                            the forward's output for the same arguments
+ *   lse                 in : [batch][heads][seqlen] fp32 from fa_forward
+ *   dq, dk, dv          out: [batch][seqlen][heads][headdim], dtype
+ *   workspace           scratch of at least fa_backward_workspace_size() bytes,
+ *                       16-byte aligned; its contents on entry are ignored
+ * The mask arguments must match the forward call that produced out and lse.
+ * The result is deterministic: dQ is produced by its own pass over the keys
+ * (no atomics), dK and dV by a pass over the queries.
+ */
+fa_status_t fa_backward(const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv,
+                        const int32_t* seqlens_k,
+                        int batch, int heads, int seqlen, int headdim,
+                        float softmax_scale, int causal,
+                        int window_left, int window_right,
+                        fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Static English name of a status code. Never NULL. */
+const char* fa_status_string(fa_status_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the thread's next call into the library. */
+const char* fa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects bad arguments before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_35_amd import binding as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH),
+                                reason="libfa_mi355x.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_status_string",
+         "fa_last_error_message"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fb.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(n for n, _, _ in fb.SIGNATURES) == declared_functions()
+
+
+def test_status_strings():
+    lib = fb.load_library()
+    for code in range(5):
+        assert lib.fa_status_string(code)
+    assert lib.fa_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, seqlens=None, B=1, H=1, N=16, D=64,
+             scale=0.125, causal=0, wl=-1, wr=-1, dtype=fb.FA_DTYPE_BF16)
+    a.update(kw)
+    return lib.fa_forward(a["q"], a["k"], a["v"], a["out"], a["lse"], a["seqlens"], a["B"],
+                          a["H"], a["N"], a["D"], a["scale"], a["causal"], a["wl"], a["wr"],
+                          a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=0), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(H=-1), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(N=0), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(N=(1 << 24) + 1), fb.FA_ERR_INVALID_ARG, "seqlen"),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 8), fb.FA_ERR_INVALID_ARG, "2^31"),
+    (dict(D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
+    (dict(dtype=7), fb.FA_ERR_UNSUPPORTED, "dtype"),
+    (dict(scale=float("nan")), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(scale=0.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(scale=-1.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(wl=-2), fb.FA_ERR_INVALID_ARG, "window"),
+    (dict(wr=-5), fb.FA_ERR_INVALID_ARG, "window"),
+    (dict(q=None), fb.FA_ERR_INVALID_ARG, "q is null"),
+    (dict(lse=None), fb.FA_ERR_INVALID_ARG, "lse is null"),
+    (dict(v=FAKE + 8), fb.FA_ERR_INVALID_ARG, "v is not 16-byte aligned"),
+    (dict(seqlens=FAKE + 2), fb.FA_ERR_INVALID_ARG, "seqlens_k"),
+])
+def test_forward_rejects_before_launch(kw, status, needle):
+    lib = fb.load_library()
+    assert fwd(lib, **kw) == status
+    assert needle in lib.fa_last_error_message().decode()
+
+
+def bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             seqlens=None, B=2, H=3, N=100, D=64, scale=0.125, causal=1, wl=-1, wr=-1,
+             dtype=fb.FA_DTYPE_BF16, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_backward(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"],
+                           a["dk"], a["dv"], a["seqlens"], a["B"], a["H"], a["N"], a["D"],
+                           a["scale"], a["causal"], a["wl"], a["wr"], a["dtype"], a["ws"],
+                           a["wsb"], None)
+
+
+def test_workspace_size():
+    lib = fb.load_library()
+    need = lib.fa_backward_workspace_size(2, 3, 100, 64, fb.FA_DTYPE_BF16)
+    assert need >= 2 * 3 * 100 * 4 and need % 256 == 0
+    assert lib.fa_backward_workspace_size(0, 3, 100, 64, fb.FA_DTYPE_BF16) == 0
+    assert lib.fa_backward_workspace_size(2, 3, 100, 80, fb.FA_DTYPE_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(ws=None), fb.FA_ERR_WORKSPACE, "workspace"),
+    (dict(wsb=16), fb.FA_ERR_WORKSPACE, "workspace"),
+    (dict(ws=FAKE + 4), fb.FA_ERR_INVALID_ARG, "workspace"),
+    (dict(dout=None), fb.FA_ERR_INVALID_ARG, "dout is null"),
+    (dict(dk=FAKE + 2), fb.FA_ERR_INVALID_ARG, "dk is not 16-byte aligned"),
+    (dict(D=32), fb.FA_ERR_UNSUPPORTED, "headdim"),
+    (dict(dtype=fb.FA_DTYPE_F32), fb.FA_ERR_UNSUPPORTED, "bf16"),
+    (dict(wl=-3), fb.FA_ERR_INVALID_ARG, "window"),
+])
+def test_backward_rejects_before_launch(kw, status, needle):
+    lib = fb.load_library()
+    assert bwd(lib, **kw) == status
+    assert needle in lib.fa_last_error_message().decode()
+
+
+def test_binding_without_library_fails_loudly(tmp_path):
+    with pytest.raises(fb.FaError):
+        fb.load_library(str(tmp_path / "missing.so"))
