@@ -25,12 +25,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall",
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc", "-munsafe-fp-atomics"]
+# Per-source extras. The forward keeps MFMA results in arch VGPRs: it reads
+# every score accumulator with VALU ops, and the accumulator-register form
+# would add a copy per element.
+EXTRA = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     path = os.path.join(HERE, "csrc", src)
     obj = os.path.join(BUILD_DIR, src + ".o")
     cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"])
+    cmd += EXTRA.get(src, [])
     cmd += ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # The host pass does not know the packed-fp32 feature name; that note is harmless.

@@ -15,6 +15,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ int key_len(const MaskParams& m, int b, int N) {
   if (m.seqlens_k == nullptr) return N;
@@ -39,6 +41,12 @@ __device__ __forceinline__ bool block_all_visible(const MaskParams& m, int kl, i
   if (m.wl >= 0 && ka < qb - m.wl) return false;
   if (m.wr >= 0 && kb > qa + m.wr) return false;
   return true;
+}
+
+// Keys visible to query i form the span [lo, hi] (empty when hi < lo).
+__device__ __forceinline__ void visible_span(const MaskParams& m, int kl, int i, int& lo, int& hi) {
+  lo = m.wl >= 0 ? i - m.wl : 0;
+  hi = m.wr >= 0 ? min(kl - 1, i + m.wr) : kl - 1;
 }
 
 __device__ __forceinline__ bool visible(const MaskParams& m, int kl, int i, int j) {
@@ -105,6 +113,13 @@ __device__ __forceinline__ f32x16_t mfma_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
 }
 __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read of 4 x 16-bit values (gfx950 ds_read_b64_tr_b16). In
+// each group of 16 lanes, the lanes address a 16 x 4 block (one 8-byte row
+// per lane); lane i receives element (4 e + i / 4, i % 4) for e = 0..3.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
 }
 
 template <typename T>

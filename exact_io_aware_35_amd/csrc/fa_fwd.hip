@@ -1,231 +1,294 @@
 // fa_fwd.hip -- tiled exact-attention forward for gfx950.
 //
-// One work-group per (batch, head, block of BM query rows); each wave owns 32
-// query rows, so the work is parallel along the sequence as well as over
-// batch and heads (interview guide "FlashAttention 深入", section
-// "v1 → v2 → v3 演进", the v2 row). The key/value sequence is streamed in tiles
-// of BN keys through LDS (double-buffered) and never leaves the chip as an
-// N x N matrix (l189.com from-scratch article, §2.1/§2.4 tiling; §3.1 loop
-// over key blocks inside a query block).
+// One work-group per (batch, head, block of query rows); the work is parallel
+// along the sequence as well as over batch and heads (interview guide
+// "FlashAttention 深入", section "v1 → v2 → v3 演进", the v2 row). The key/value
+// sequence is streamed in tiles through LDS and never leaves the chip as an
+// N x N matrix (l189.com from-scratch article, §2.1/§2.4 tiling; §3.1 loop over
+// key blocks inside a query block).
 //
 // Per tile, a wave computes S^T = K Q^T on MFMA with fp32 accumulation, so
-// that each lane holds the scores of ONE query row (lane % 32) for 16 keys per
-// 32-key block; the row max is then an in-lane max plus one exchange between
-// the two 32-lane halves. The online softmax (from-scratch article §2.2; the
-// interview guide's "Online Softmax" section) keeps, per row, a reference max
-// M (log2 domain) and the sum l of 2^(c2 s - M); the partial output and l are
-// rescaled by 2^(M_old - M_new) when M changes. Rescaling is done lazily: M is
-// only raised when some row's tile max exceeds it by more than 8 (log2 units),
-// so P values stay <= 2^8; O and l always share the same M, so the result is
-// unchanged up to rounding. O^T += V^T P^T then runs on MFMA with P packed to
-// bf16 straight from the score accumulators; V is stored transposed in LDS,
-// with the key order inside each 16-key group permuted to match the order in
-// which the accumulator holds keys.
+// that each lane holds the scores of one query row for 16 keys per 32-key
+// block; the row max is then an in-lane max plus one exchange between the two
+// 32-lane halves. The online softmax (from-scratch article §2.2; the interview
+// guide's "Online Softmax" section) keeps, per row, a reference max M (log2
+// domain) and the sum l of 2^(c2 s - M); the partial output and l are rescaled
+// by 2^(M_old - M_new) when M changes. Rescaling is lazy: M is only raised when
+// some row's tile max exceeds it by more than 8 (log2 units), so P values stay
+// <= 2^8; O and l always share the same M, so the result is unchanged up to
+// rounding. O^T += V^T P^T then runs on MFMA with P packed to bf16 straight
+// from the score accumulators, in the key order the accumulator holds them.
 //
 // Epilogue: O = O_acc / l rounded to the output dtype; LSE = (M + log2 l) ln 2
 // (from-scratch article §3.1 LSE statistic, §5.2 fp32 statistics).
+
+#include <type_traits>
 
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 
-// Position of key k inside a transposed V row: within every 16-key group,
-// bits 2 and 3 of the index are swapped, so the 8 keys one lane feeds to a
-// 32x32x16 MFMA (keys 8a + 4h + c of the group, a in {0,1}, c in 0..3, h the
-// lane's half) sit at positions 8h + 4a + c, contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
+// XOR swizzle of the 16-byte chunks of a K or V row in LDS. Chunk c of row r
+// is stored at position c ^ swz(r). With it, the two LDS read patterns of the
+// kernel are free of bank conflicts: 16 consecutive rows reading one chunk
+// (K as an MFMA operand) and 4 consecutive rows x 4 consecutive chunks (V
+// read transposed). swz only depends on the low 4 bits of the row.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int D, int NW, int BN>
-struct FwdBf16Cfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BM = NW * 32;
-  static constexpr int KSTR = D + 8;   // K row stride in LDS (elements); +16 B spreads rows over banks
-  static constexpr int VSTR = BN + 8;  // transposed-V row stride (elements)
-  static constexpr int KTILE = BN * KSTR;
-  static constexpr int VTILE = D * VSTR;
-  static constexpr int KCH = BN * D / 8 / NT;  // 16-byte K chunks per thread per tile
-  static constexpr int KPT = BN * D / 8 / NT;  // keys per thread when staging V
-  static constexpr int KGROUPS = BN / KPT;
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(KPT == 2 || KPT == 4, "V staging handles 2 or 4 keys per thread");
+template <int D, int BN_ = 64, int NW_ = 8, int QW_ = 32>
+struct FwdCfg {
+  static constexpr int NW = NW_;               // waves per work-group
+  static constexpr int QW = QW_;               // query rows per wave
+  static constexpr int BM = NW * QW;           // query rows per work-group
+  static constexpr int BN = BN_;               // keys per tile
+  static constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * D * 2;      // bytes of one K or V tile
+  static constexpr int LPW = TILE / 1024 / NW; // 1 KiB direct-to-LDS loads per wave per matrix
+  static constexpr int QB = QW / 32, KB = BN / 32, DB = D / 32, KS = BN / 16, DS = D / 16;
+  static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
 };
 
-template <int D, int NW, int BN>
-__global__ void __launch_bounds__(NW * 64) fwd_bf16_kernel(FwdParams p) {
-  using C = FwdBf16Cfg<D, NW, BN>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::KTILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::VTILE];
+// bf16 forward. One work-group = 4 waves x 64 query rows. K and V tiles are
+// copied global -> LDS by the 16-byte direct-to-LDS loads (no staging
+// registers), double-buffered: the copy of tile t+1 is in flight while tile t
+// is computed. Rows past the end of the sequence are clamped onto the last
+// row (their scores are masked to -inf, so their values never contribute).
+//
+// Per tile and wave: S^T = K Q^T on 32x32x16 MFMA (each lane holds the scores
+// of two query rows, ln and 32 + ln, for 16 keys per 32-key block); online
+// softmax with a lazily raised reference max; O^T += V^T P^T with the V^T
+// operand read by ds_read_b64_tr_b16 (lane i of a 16-lane group receives
+// element (4e + i/4, i%4) of the 16 x 4 block the group addresses, so each
+// lane points at 4 values of one key row and gets 4 keys of one d column).
+template <int D>
+__global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams p) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];  // [buf][K | V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, hf = lane >> 5;
-  int bh, qb;
-  map_block(p.B * p.H, p.nqb, p.xcd_groups, p.longest_first, bh, qb);
+  int bh, qblk;
+  map_block(p.B * p.H, p.nqb, p.xcd_groups, p.longest_first, bh, qblk);
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
-  const int q0 = qb * C::BM;
+  const int q0 = qblk * C::BM;
   const int kl = key_len(p.mask, b, N);
-  const size_t rs = (size_t)p.H * D;                    // elements between sequence positions
+  const int rs = p.H * D;                               // elements between sequence positions
   const size_t base = ((size_t)b * N * p.H + h) * D;    // element (b, 0, h, 0)
   const __bf16* Q = (const __bf16*)p.q + base;
-  const __bf16* K = (const __bf16*)p.k + base;
-  const __bf16* V = (const __bf16*)p.v + base;
+  const char* Kg = (const char*)((const __bf16*)p.k + base);
+  const char* Vg = (const char*)((const __bf16*)p.v + base);
   __bf16* O = (__bf16*)p.o + base;
 
-  const int qi = q0 + wave * 32 + ln;                   // this lane's query row
+  const int wq0 = q0 + wave * C::QW;                    // first query row of this wave
   int klo, khi;
   key_range(p.mask, kl, q0, min(q0 + C::BM, N) - 1, klo, khi);
-  const int t0 = klo / BN, t1 = (khi + BN - 1) / BN;
-  const int wq0 = q0 + wave * 32, wq1 = min(wq0 + 31, N - 1);
+  const int t0 = klo / C::BN, t1 = (khi + C::BN - 1) / C::BN;
+  const int wq1 = min(wq0 + C::QW - 1, N - 1);
   int wklo = 0, wkhi = 0;
   if (wq0 <= wq1) key_range(p.mask, kl, wq0, wq1, wklo, wkhi);
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qi][16s + 8hf .. +8).
-  bf16x8_t qf[D / 16];
+  // Q as the B operand of S^T = K Q^T: qf[qb][s] = Q[wq0 + 32 qb + ln][16 s + 8 hf ..+8).
+  bf16x8_t qf[C::QB][C::DS];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (qi < N) qf[s] = ld_global<bf16x8_t>(Q + (size_t)qi * rs + 16 * s + 8 * hf);
-    else qf[s] = bf16x8_t{};
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int row = min(wq0 + 32 * qb + ln, N - 1);     // rows past N are computed, never stored
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) qf[qb][s] = ld_global<bf16x8_t>(Q + (size_t)row * rs + 16 * s + 8 * hf);
   }
 
-  f32x16_t oacc[D / 32];
+  // Direct-to-LDS copy: load j of this wave fills LDS chunks
+  // [(wave * LPW + j) * 64, +64) of a tile; lane -> (row, swizzled chunk).
+  int lrow[C::LPW], lcol[C::LPW];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) oacc[d] = f32x16_t{};
-  float m_ref = -INFINITY;  // reference max, log2 domain
-  float l_part = 0.f;       // this lane's half of the row sum
-
-  u32x4_t kreg[C::KCH];
-  u32x4_t vreg[C::KPT];
-  const int vkg = tid % C::KGROUPS, vdc = tid / C::KGROUPS;
-
-  auto load_tile = [&](int t) {
-    const int kt = t * BN;
+  for (int j = 0; j < C::LPW; ++j) {
+    const int u = (wave * C::LPW + j) * 64 + lane;
+    const int row = u / C::CPR, pos = u % C::CPR;
+    lrow[j] = row;
+    lcol[j] = (pos ^ swz<D>(row)) * 16;
+  }
+  const int rs2 = rs * 2;
+  auto issue_tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kt = t * C::BN;
+    const int lim = N - 1 - kt;
+    const char* kg = Kg + (size_t)kt * rs2;
+    const char* vg = Vg + (size_t)kt * rs2;
+    char* kd = smem + (2 * buf) * C::TILE + wave * C::LPW * 1024;
+    char* vd = smem + (2 * buf + 1) * C::TILE + wave * C::LPW * 1024;
 #pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + C::NT * r, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = kt + row;
-      kreg[r] = key < N ? ld_global<u32x4_t>(K + (size_t)key * rs + col) : u32x4_t{};
-    }
-#pragma unroll
-    for (int r = 0; r < C::KPT; ++r) {
-      const int key = kt + vkg * C::KPT + r;
-      vreg[r] = key < N ? ld_global<u32x4_t>(V + (size_t)key * rs + vdc * 8) : u32x4_t{};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + C::NT * r, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4_t*)&sK[buf][row * C::KSTR + col] = kreg[r];
-    }
-    const int kpos = vt_pos(vkg * C::KPT);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      __bf16* lo = &sV[buf][(vdc * 8 + 2 * e) * C::VSTR + kpos];
-      __bf16* hi = lo + C::VSTR;
-      if constexpr (C::KPT == 4) {
-        *(u32x2_t*)lo = u32x2_t{(vreg[0][e] & 0xffffu) | (vreg[1][e] << 16),
-                                (vreg[2][e] & 0xffffu) | (vreg[3][e] << 16)};
-        *(u32x2_t*)hi = u32x2_t{(vreg[0][e] >> 16) | (vreg[1][e] & 0xffff0000u),
-                                (vreg[2][e] >> 16) | (vreg[3][e] & 0xffff0000u)};
-      } else {
-        *(uint32_t*)lo = (vreg[0][e] & 0xffffu) | (vreg[1][e] << 16);
-        *(uint32_t*)hi = (vreg[0][e] >> 16) | (vreg[1][e] & 0xffff0000u);
-      }
+    for (int j = 0; j < C::LPW; ++j) {
+      const unsigned off = (unsigned)(min(lrow[j], lim) * rs2 + lcol[j]);
+      __builtin_amdgcn_global_load_lds((const void*)(kg + off),
+                                       (__attribute__((address_space(3))) void*)(kd + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg + off),
+                                       (__attribute__((address_space(3))) void*)(vd + j * 1024), 16, 0, 0);
     }
   };
 
-  if (t0 < t1) {
-    load_tile(t0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    const bool more = t + 1 < t1;
-    if (more) load_tile(t + 1);
-    const int kt = t * BN;
-    if (kt < wkhi && kt + BN > wklo) {
-      // S^T = K Q^T. sacc[kb][i] is the score of query qi and key
-      // kt + 32 kb + 8 (i / 4) + 4 hf + i % 4.
-      f32x16_t sacc[BN / 32];
+  // LDS read offsets (bytes within a tile). K operand for d-step s: row ln
+  // (+32 kb), logical chunk 2 s + hf. V^T operand for (d-block db, half t of
+  // the 16-key step): lane r of 16-lane group g addresses key row
+  // 8 t + 4 (g / 2) + r / 4 (+16 ks) at d = 32 db + 16 (g % 2) + 4 (r % 4).
+  int koff[C::DS];
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        sacc[kb] = f32x16_t{};
+  for (int s = 0; s < C::DS; ++s) koff[s] = (ln * C::CPR + ((2 * s + hf) ^ swz<D>(ln))) * 16;
+  int voff[C::DB][2];
+  {
+    const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const bf16x8_t a = *(const bf16x8_t*)&sK[buf][(32 * kb + ln) * C::KSTR + 16 * s + 8 * hf];
-          sacc[kb] = mfma_bf16(a, qf[s], sacc[kb]);
-        }
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 8 * t + 4 * (g >> 1) + (r >> 2);
+        const int col = 32 * db + 16 * (g & 1) + 4 * (r & 3);
+        voff[db][t] = (row * C::CPR + ((col >> 3) ^ swz<D>(row))) * 16 + ((col >> 2) & 1) * 8;
       }
-      if (!block_all_visible(p.mask, kl, wq0, wq1, kt, kt + BN - 1)) {
+  }
+
+  f32x16_t oacc[C::DB][C::QB];
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
+  for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) oacc[d][qb] = f32x16_t{};
+  float m_ref[C::QB], l_part[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) { m_ref[qb] = -INFINITY; l_part[qb] = 0.f; }
+
+  auto compute = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const char* sk = smem + (2 * buf) * C::TILE;
+    const char* sv = smem + (2 * buf + 1) * C::TILE;
+    const int kt = t * C::BN;
+    if (!(kt < wkhi && kt + C::BN > wklo)) return;  // wave-uniform: no visible key here
+    f32x16_t sacc[C::KB][C::QB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        const bf16x8_t a = *(const bf16x8_t*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = mfma_bf16(a, qf[qb][s], sacc[kb][qb]);
+      }
+    if (!block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1)) {
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        int lo, hi;
+        visible_span(p.mask, kl, wq0 + 32 * qb + ln, lo, hi);
+        const int jb = kt + 4 * hf;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = kt + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!visible(p.mask, kl, qi, j)) sacc[kb][i] = -INFINITY;
+            const int j = jb + 32 * kb + 8 * (i >> 2) + (i & 3);
+            sacc[kb][qb][i] = (j >= lo) & (j <= hi) ? sacc[kb][qb][i] : -INFINITY;
           }
       }
+    }
+    float mt[C::QB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      const float mt = half_max(mx) * p.scale_log2;
-      if (__ballot(mt > m_ref + 8.f)) {  // wave-uniform
-        const float m_new = fmaxf(m_ref, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
-        l_part *= alpha;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
+      mt[qb] = half_max(mx) * p.scale_log2;
+      grow |= mt[qb] > m_ref[qb] + 8.f;
+    }
+    if (__ballot(grow)) {  // wave-uniform
 #pragma unroll
-        for (int d = 0; d < D / 32; ++d) oacc[d] *= alpha;
-        m_ref = m_new;
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const float m_new = fmaxf(m_ref[qb], mt[qb]);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref[qb] - m_new);
+        l_part[qb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) oacc[d][qb] *= alpha;
+        m_ref[qb] = m_new;
       }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      u32x4_t pk[BN / 16];  // P in bf16, 8 keys per 16-byte operand
+    }
+    u32x4_t pk[C::QB][C::KS];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const float m_use = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
       float rsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0 = exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -m_use));
-          const float p1 = exp2_fast(fmaf(sacc[kb][i + 1], p.scale_log2, -m_use));
-          rsum += p0 + p1;
-          pk[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+          const float p0 = exp2_fast(fmaf(sacc[kb][qb][i], p.scale_log2, -m_use));
+          const float p1 = exp2_fast(fmaf(sacc[kb][qb][i + 1], p.scale_log2, -m_use));
+          rsum += p0 + p1;  // fp32 sum of the unrounded P (LSE must hold to 1e-3 on short rows)
+          pk[qb][2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
         }
-      l_part += rsum;
-      // O^T += V^T P^T: A = transposed V rows (d), B = P from the accumulators.
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks) {
-          const bf16x8_t a = *(const bf16x8_t*)&sV[buf][(32 * d + ln) * C::VSTR + 16 * ks + 8 * hf];
-          oacc[d] = mfma_bf16(a, __builtin_bit_cast(bf16x8_t, pk[ks]), oacc[d]);
-        }
+      l_part[qb] += rsum;
     }
-    if (more) store_tile(buf ^ 1);
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const char* vbase = sv + ks * 16 * C::CPR * 16;
+        const u32x2_t lo = lds_read_tr16(vbase + voff[d][0]);
+        const u32x2_t hi = lds_read_tr16(vbase + voff[d][1]);
+        const u32x4_t a = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+          oacc[d][qb] = mfma_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, pk[qb][ks]),
+                                  oacc[d][qb]);
+      }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // Tile t0 + 2i lives in buffer 0, t0 + 2i + 1 in buffer 1. The copy of the
+  // next tile is issued before the current one is computed; the wait and the
+  // barrier after the compute make it visible and free the buffer just read.
+  if (t0 < t1) issue_tile(t0, B0{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    issue_tile(t + 1, B1{});
+    compute(t, B0{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < t1) issue_tile(t + 2, B0{});
+    compute(t + 1, B1{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if (t < t1) compute(t, B0{});
 
-  const float l = half_sum(l_part);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (qi < N) {
-    __bf16* orow = O + (size_t)qi * rs;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int qi = wq0 + 32 * qb + ln;
+    const float l = half_sum(l_part[qb]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (qi < N) {
+      __bf16* orow = O + (size_t)qi * rs;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * d + 8 * g + 4 * hf;
-        *(u32x2_t*)(orow + col) =
-            u32x2_t{pack_bf16x2(oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv),
-                    pack_bf16x2(oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv)};
-      }
-    if (hf == 0)
-      p.lse[((size_t)b * p.H + h) * N + qi] =
-          l > 0.f ? (m_ref + log2_fast(l)) * 0.69314718055994531f : -INFINITY;
+      for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * d + 8 * g + 4 * hf;
+          *(u32x2_t*)(orow + col) =
+              u32x2_t{pack_bf16x2(oacc[d][qb][4 * g] * inv, oacc[d][qb][4 * g + 1] * inv),
+                      pack_bf16x2(oacc[d][qb][4 * g + 2] * inv, oacc[d][qb][4 * g + 3] * inv)};
+        }
+      if (hf == 0)
+        p.lse[((size_t)b * p.H + h) * N + qi] =
+            l > 0.f ? (m_ref[qb] + log2_fast(l)) * 0.69314718055994531f : -INFINITY;
+    }
   }
 }
 
@@ -369,10 +432,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
 
 // ---------------------------------------------------------------- launchers
 
-static constexpr int kFwdWaves = 4;
-static constexpr int kFwdBN = 64;
-
-int fwd_block_rows(int dtype_is_f32) { return dtype_is_f32 ? 128 : kFwdWaves * 32; }
+int fwd_block_rows(int dtype_is_f32) { return dtype_is_f32 ? 128 : FwdCfg<128>::BM; }
 
 hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
   const dim3 grid(p.B * p.H * p.nqb);
@@ -380,11 +440,9 @@ hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_
     if (headdim == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(256), 0, stream, p);
   } else {
-    constexpr int NT = kFwdWaves * 64;
-    if (headdim == 64)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdWaves, kFwdBN>), grid, dim3(NT), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdWaves, kFwdBN>), grid, dim3(NT), 0, stream, p);
+    static_assert(FwdCfg<64>::BM == FwdCfg<128>::BM, "one block height for both head dims");
+    if (headdim == 64) hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, dim3(FwdCfg<64>::NW * 64), 0, stream, p);
+    else hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, dim3(FwdCfg<128>::NW * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
