@@ -9,6 +9,8 @@ the stream it runs on, and the fp64 CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --extra      # also write fwd/bwd lines for every workload
+    python bench.py --copy-mib 256   # also run a plain 256 MiB device copy (counter calibration)
+    python bench.py --summarize DIR_FETCH DIR_WRITE DIR_STATS   # write profiles/ summaries
 
 Only one GPU is used: --gpus N with N > 1 exits with a message.
 """
@@ -99,6 +101,65 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def plain_copy(mib, reps=5):
+    """A plain device-to-device copy of `mib` MiB, the calibration kernel for
+    the HBM byte counters (its bytes moved are known exactly)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_means(csv_path, counter):
+    """Per-dispatch mean of `counter` for each kernel name in a rocprofv3
+    counter_collection.csv."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize(fetch_dir, write_dir, stats_dir, copy_mib, cmds):
+    """Turn rocprofv3 outputs into the committed profile summaries."""
+    import glob
+    fcsv = glob.glob(os.path.join(fetch_dir, "**", "*counter_collection.csv"), recursive=True)[0]
+    wcsv = glob.glob(os.path.join(write_dir, "**", "*counter_collection.csv"), recursive=True)[0]
+    fetch = _counter_means(fcsv, "FETCH_SIZE")
+    write = _counter_means(wcsv, "WRITE_SIZE")
+    attn = [k for k in fetch if "fwd_bf16_kernel" in k][0]
+    copy = [k for k in fetch if "fwd_bf16_kernel" not in k and "opy" in k or "elementwise" in k]
+    copy = max(copy, key=lambda k: fetch[k])
+    known = copy_mib * (1 << 20)
+    f_scale = known / (fetch[copy] * 1024.0)
+    w_scale = known / (write[copy] * 1024.0)
+    hbm_read = fetch[attn] * 1024.0 * f_scale
+    hbm_write = write[attn] * 1024.0 * w_scale
+    out = {"kernel": attn, "workload": "fwd_bf16_b2h8n4096d128",
+           "kernel_source_hash": kernel_source_hash(),
+           "fetch_size_kib_per_dispatch": fetch[attn], "write_size_kib_per_dispatch": write[attn],
+           "copy_kernel": copy, "copy_bytes": known,
+           "copy_fetch_kib": fetch[copy], "copy_write_kib": write[copy],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": hbm_read, "hbm_write_bytes_per_launch": hbm_write,
+           "hbm_bytes_per_launch": hbm_read + hbm_write,
+           "commands": cmds}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    scsv = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    lines = open(scsv).read().strip().splitlines()
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_fwd_bf16_b2h8n4096d128.txt"), "w") as f:
+        f.write("rocprofv3 --kernel-trace --stats summary of the forward on B2 H8 N4096 D128 bf16\n")
+        f.write("command: " + cmds["stats"] + "\n\n")
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle on (batch, head) slices of the same inputs until about
     `seconds` of CPU time have passed; returns TFLOP/s over the slices done."""
@@ -141,7 +202,7 @@ def run_workload(w, steps, warmup, backward=False):
     out = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.seqlen), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, window=w.window, softmax_scale=w.softmax_scale, seqlens_k=sk)
-    fwd = lambda: fa.forward(q, k, v, out=out, lse=lse, **kw)
+    fwd = fa.prepare_forward(q, k, v, out, lse, **kw)
     t_f = time_gpu(fwd, steps, warmup)
     t_b = None
     if backward:
@@ -164,7 +225,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true",
                     help="also time fwd/bwd of every workload; lines go to stderr")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB")
+    ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 output directories")
     args = ap.parse_args()
+    if args.summarize:
+        cmd = "rocprofv3 {opts} -- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-mib 256"
+        summarize(*args.summarize, copy_mib=256,
+                  cmds={"fetch": cmd.format(opts="--pmc FETCH_SIZE --output-format csv"),
+                        "write": cmd.format(opts="--pmc WRITE_SIZE --output-format csv"),
+                        "stats": cmd.format(opts="--kernel-trace --stats --output-format csv")})
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this build measures the single-GPU kernel "
@@ -186,9 +258,10 @@ def main():
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    # One kernel per step: its average launch duration is the timed region's
-    # mean; the per-launch event pairs are reported beside it.
-    kernel_tflops = flops / (ms * 1e-3) / 1e12
+    # The forward is one kernel; its average launch duration comes from an
+    # event pair around each launch on the stream it runs on (the timed
+    # region's mean also holds the host-side launch gaps).
+    kernel_tflops = flops / (mean_ms * 1e-3) / 1e12
     traffic = load_traffic()
     line = {
         "metric": METRIC,
@@ -222,6 +295,8 @@ def main():
             if tb is not None:
                 rec.update(bwd_ms=round(tb, 4), bwd_tflops=round(2.5 * ff / tb / 1e9, 2))
             print("extra: " + json.dumps(rec), file=sys.stderr, flush=True)
+    if args.copy_mib:
+        plain_copy(args.copy_mib)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -122,6 +122,40 @@ def forward(q, k, v, causal=False, window=(-1, -1), softmax_scale=None, seqlens_
     return out, lse
 
 
+class PreparedCall:
+    """An entry point with its arguments marshalled once.
+
+    Calling it re-issues the same launch on the same stream, skipping the
+    per-call checks and conversions of forward()/backward(); the tensors it
+    was built from must stay alive and keep their storage.
+    """
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep  # tensors whose storage the raw pointers refer to
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != FA_OK:
+            _check(load_library(), st)
+
+
+def prepare_forward(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_scale=None,
+                    seqlens_k=None, stream=None):
+    """forward() with every argument marshalled once; returns a callable."""
+    lib = load_library()
+    B, N, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    args = (_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+            _dev_ptr(lse, "lse"), _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale,
+            int(bool(causal)), int(window[0]), int(window[1]), _dtype_code(q),
+            _stream_handle(stream, q.device))
+    call = PreparedCall(lib.fa_forward, args, (q, k, v, out, lse, seqlens_k))
+    call()  # surfaces argument errors now
+    return call
+
+
 def workspace_size(batch, heads, seqlen, headdim, dtype_code=FA_DTYPE_BF16):
     return int(load_library().fa_backward_workspace_size(batch, heads, seqlen, headdim, dtype_code))
 

@@ -101,7 +101,7 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* out, f
   p.mask.wl = wl;
   p.mask.wr = wr;
   p.B = batch; p.H = heads; p.N = seqlen;
-  const int bm = fa::fwd_block_rows(f32);
+  const int bm = fa::fwd_block_rows(f32, headdim);
   p.nqb = (seqlen + bm - 1) / bm;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.xcd_groups = (batch * heads) % 8 == 0 ? 1 : 0;

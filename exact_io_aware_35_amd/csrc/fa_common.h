@@ -122,6 +122,19 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16-byte buffer load straight into LDS: lane i of the wave writes
+// lds + 16 i with the 16 bytes at voffset + soffset of the buffer.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voffset,
+                                                  int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, soffset, 0, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ T ld_global(const void* p) { return *reinterpret_cast<const T*>(p); }
 

@@ -24,6 +24,7 @@
 
 #include <type_traits>
 
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -40,7 +41,17 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int D, int BN_ = 64, int NW_ = 8, int QW_ = 32>
+// Tile shape per head dimension, chosen by measurement on MI355X: at D = 128
+// eight waves share each K/V tile (256 query rows per work-group); at D = 64
+// two independent 4-wave work-groups per CU do better (their barriers do not
+// keep the two waves of a SIMD in lockstep).
+template <int D>
+struct FwdShape {
+  static constexpr int NW = D == 128 ? 8 : 4;
+  static constexpr int BN = 64;
+};
+
+template <int D, int BN_ = FwdShape<D>::BN, int NW_ = FwdShape<D>::NW, int QW_ = 32>
 struct FwdCfg {
   static constexpr int NW = NW_;               // waves per work-group
   static constexpr int QW = QW_;               // query rows per wave
@@ -50,6 +61,7 @@ struct FwdCfg {
   static constexpr int TILE = BN * D * 2;      // bytes of one K or V tile
   static constexpr int LPW = TILE / 1024 / NW; // 1 KiB direct-to-LDS loads per wave per matrix
   static constexpr int QB = QW / 32, KB = BN / 32, DB = D / 32, KS = BN / 16, DS = D / 16;
+  static constexpr int NBUF = 2;               // K/V tile buffers in LDS
   static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
 };
 
@@ -68,9 +80,10 @@ struct FwdCfg {
 template <int D>
 __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];  // [buf][K | V]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::NBUF * C::TILE];  // [buf][K | V]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave logic scalar
   const int ln = lane & 31, hf = lane >> 5;
   int bh, qblk;
   map_block(p.B * p.H, p.nqb, p.xcd_groups, p.longest_first, bh, qblk);
@@ -102,32 +115,31 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     for (int s = 0; s < C::DS; ++s) qf[qb][s] = ld_global<bf16x8_t>(Q + (size_t)row * rs + 16 * s + 8 * hf);
   }
 
-  // Direct-to-LDS copy: load j of this wave fills LDS chunks
-  // [(wave * LPW + j) * 64, +64) of a tile; lane -> (row, swizzled chunk).
-  int lrow[C::LPW], lcol[C::LPW];
+  // Direct-to-LDS copy through buffer loads: load j of this wave fills LDS
+  // chunks [(wave * LPW + j) * 64, +64) of a tile; lane -> (row, swizzled
+  // chunk). The per-lane byte offset is the same for every tile; the tile's
+  // first row goes in the scalar offset. Rows at or past N lie beyond the
+  // buffer's last byte and read as zero (their scores are masked anyway).
+  const int rs2 = rs * 2;
+  const int nbytes = ((N - 1) * rs + D) * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(Kg, nbytes);
+  const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(Vg, nbytes);
+  int loff[C::LPW];
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int u = (wave * C::LPW + j) * 64 + lane;
     const int row = u / C::CPR, pos = u % C::CPR;
-    lrow[j] = row;
-    lcol[j] = (pos ^ swz<D>(row)) * 16;
+    loff[j] = row * rs2 + (pos ^ swz<D>(row)) * 16;
   }
-  const int rs2 = rs * 2;
   auto issue_tile = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int kt = t * C::BN;
-    const int lim = N - 1 - kt;
-    const char* kg = Kg + (size_t)kt * rs2;
-    const char* vg = Vg + (size_t)kt * rs2;
+    const int soff = t * C::BN * rs2;
     char* kd = smem + (2 * buf) * C::TILE + wave * C::LPW * 1024;
     char* vd = smem + (2 * buf + 1) * C::TILE + wave * C::LPW * 1024;
 #pragma unroll
     for (int j = 0; j < C::LPW; ++j) {
-      const unsigned off = (unsigned)(min(lrow[j], lim) * rs2 + lcol[j]);
-      __builtin_amdgcn_global_load_lds((const void*)(kg + off),
-                                       (__attribute__((address_space(3))) void*)(kd + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg + off),
-                                       (__attribute__((address_space(3))) void*)(vd + j * 1024), 16, 0, 0);
+      buffer_load_lds16(krsrc, kd + j * 1024, loff[j], soff);
+      buffer_load_lds16(vrsrc, vd + j * 1024, loff[j], soff);
     }
   };
 
@@ -159,26 +171,33 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
   float m_ref[C::QB], l_part[C::QB];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) { m_ref[qb] = -INFINITY; l_part[qb] = 0.f; }
+  bool m_finite = false;  // wave-uniform: every row of the wave has a finite M
 
-  auto compute = [&](int t, auto bufc) {
+  // S^T of the tile a wave is working on, and whether it holds any key the
+  // wave's rows may see (wave-uniform).
+  f32x16_t sacc[C::KB][C::QB];
+  bool sact = false;
+
+  // start(t): S^T = K(t) Q^T on MFMA, masked on tiles that cross a mask edge.
+  auto start = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const char* sk = smem + (2 * buf) * C::TILE;
-    const char* sv = smem + (2 * buf + 1) * C::TILE;
     const int kt = t * C::BN;
-    if (!(kt < wkhi && kt + C::BN > wklo)) return;  // wave-uniform: no visible key here
-    f32x16_t sacc[C::KB][C::QB];
+    sact = kt < wkhi && kt + C::BN > wklo;
+    if (!sact) return;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb) {
+      bf16x8_t kop[C::DS];  // this 32-key block's K operands, read before its MFMAs
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = f32x16_t{};
+      for (int s = 0; s < C::DS; ++s) kop[s] = *(const bf16x8_t*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+      for (int qb = 0; qb < C::QB; ++qb) {
+        f32x16_t acc = f32x16_t{};
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
-        const bf16x8_t a = *(const bf16x8_t*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = mfma_bf16(a, qf[qb][s], sacc[kb][qb]);
+        for (int s = 0; s < C::DS; ++s) acc = mfma_bf16(kop[s], qf[qb][s], acc);
+        sacc[kb][qb] = acc;
       }
+    }
     if (!block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1)) {
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
@@ -194,45 +213,71 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
           }
       }
     }
-    float mt[C::QB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
-      mt[qb] = half_max(mx) * p.scale_log2;
-      grow |= mt[qb] > m_ref[qb] + 8.f;
-    }
-    if (__ballot(grow)) {  // wave-uniform
+  };
+
+  // finish(): online softmax of the held scores and O^T += V^T P^T with the
+  // V tile of the same key tile.
+  auto finish = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const char* sv = smem + (2 * buf + 1) * C::TILE;
+    if (!sact) return;
+    // P = 2^(c2 S - M) against the current reference M. Once a row has seen
+    // a visible key, M never exceeds its true running max, so its sum l >= 1
+    // and nothing underflows; the only hazard is a new score far above M.
+    // The fast path therefore skips the tile max and checks the tile's row
+    // sums instead: if any exceeds 2^64 (or M is still -inf for some row),
+    // the tile is redone on the exact path, which raises M to the running max
+    // and rescales O and l. P <= 2^64 keeps O and l far inside fp32 range.
+    u32x4_t pk[C::QB][C::KS];
+    float rsum[C::QB];
+    auto exps = [&](const float (&m_use)[C::QB]) {
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
-        const float m_new = fmaxf(m_ref[qb], mt[qb]);
+        float acc = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const float p0 = exp2_fast(fmaf(sacc[kb][qb][i], p.scale_log2, -m_use[qb]));
+            const float p1 = exp2_fast(fmaf(sacc[kb][qb][i + 1], p.scale_log2, -m_use[qb]));
+            acc += p0 + p1;  // fp32 sum of the unrounded P (LSE must hold to 1e-3 on short rows)
+            pk[qb][2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+          }
+        rsum[qb] = acc;
+      }
+    };
+    bool slow = !m_finite;
+    if (!slow) {
+      exps(m_ref);
+      bool big = false;
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) big |= !(rsum[qb] <= 0x1p64f);
+      slow = __builtin_amdgcn_readfirstlane(__ballot(big) != 0);
+    }
+    if (slow) {  // wave-uniform, rare: first visible tile, or a score far above M
+      bool fin = true;
+      float m_use[C::QB];
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
+        const float m_new = fmaxf(m_ref[qb], half_max(mx) * p.scale_log2);
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref[qb] - m_new);
         l_part[qb] *= alpha;
 #pragma unroll
         for (int d = 0; d < C::DB; ++d) oacc[d][qb] *= alpha;
         m_ref[qb] = m_new;
+        fin &= m_new != -INFINITY;
+        m_use[qb] = (m_new == -INFINITY) ? 0.f : m_new;
       }
+      m_finite = __builtin_amdgcn_readfirstlane(__ballot(!fin) == 0);
+      exps(m_use);
     }
-    u32x4_t pk[C::QB][C::KS];
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const float m_use = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
-      float rsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = exp2_fast(fmaf(sacc[kb][qb][i], p.scale_log2, -m_use));
-          const float p1 = exp2_fast(fmaf(sacc[kb][qb][i + 1], p.scale_log2, -m_use));
-          rsum += p0 + p1;  // fp32 sum of the unrounded P (LSE must hold to 1e-3 on short rows)
-          pk[qb][2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
-        }
-      l_part[qb] += rsum;
-    }
+    for (int qb = 0; qb < C::QB; ++qb) l_part[qb] += rsum[qb];
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
@@ -250,24 +295,26 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // Tile t0 + 2i lives in buffer 0, t0 + 2i + 1 in buffer 1. The copy of the
-  // next tile is issued before the current one is computed; the wait and the
-  // barrier after the compute make it visible and free the buffer just read.
-  if (t0 < t1) issue_tile(t0, B0{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  int t = t0;
-  for (; t + 1 < t1; t += 2) {
-    issue_tile(t + 1, B1{});
-    compute(t, B0{});
+  // Key tiles alternate between two LDS buffers (tile t0 + i in buffer i % 2).
+  // Each interval issues the copy of the next tile into the other buffer, then
+  // computes the current tile; the wait and barrier at its end make the next
+  // tile visible and release the buffer just read.
+  auto interval = [&](int t, auto cur, auto nxt) {
+    if (t + 1 < t1) issue_tile(t + 1, nxt);
+    start(t, cur);
+    finish(cur);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 2 < t1) issue_tile(t + 2, B0{});
-    compute(t + 1, B1{});
+  };
+  if (t0 < t1) {
+    issue_tile(t0, B0{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    for (int t = t0; t < t1; t += 2) {
+      interval(t, B0{}, B1{});
+      if (t + 1 < t1) interval(t + 1, B1{}, B0{});
+    }
   }
-  if (t < t1) compute(t, B0{});
 
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
@@ -432,7 +479,10 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
 
 // ---------------------------------------------------------------- launchers
 
-int fwd_block_rows(int dtype_is_f32) { return dtype_is_f32 ? 128 : FwdCfg<128>::BM; }
+int fwd_block_rows(int dtype_is_f32, int headdim) {
+  if (dtype_is_f32) return 128;
+  return headdim == 64 ? FwdCfg<64>::BM : FwdCfg<128>::BM;
+}
 
 hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
   const dim3 grid(p.B * p.H * p.nqb);
@@ -440,7 +490,6 @@ hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_
     if (headdim == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(256), 0, stream, p);
   } else {
-    static_assert(FwdCfg<64>::BM == FwdCfg<128>::BM, "one block height for both head dims");
     if (headdim == 64) hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, dim3(FwdCfg<64>::NW * 64), 0, stream, p);
     else hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, dim3(FwdCfg<128>::NW * 64), 0, stream, p);
   }

@@ -8,7 +8,7 @@
 namespace fa {
 
 // Rows of the query block one forward work-group owns.
-int fwd_block_rows(int dtype_is_f32);
+int fwd_block_rows(int dtype_is_f32, int headdim);
 // Enqueue the forward on `stream`; p.nqb must equal ceil(N / fwd_block_rows()).
 hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream);
 
