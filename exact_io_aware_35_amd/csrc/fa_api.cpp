@@ -40,6 +40,12 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
     return fail(FA_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
   if (headdim != 64 && headdim != 128)
     return fail(FA_ERR_UNSUPPORTED, "headdim %d is not supported (64 or 128)", headdim);
+  // Kernels address one (batch, head) slice with 32-bit byte offsets (buffer
+  // loads take a 32-bit offset); one key tile of slack covers the prefetch.
+  const long long esize = dtype == FA_DTYPE_F32 ? 4 : 2;
+  if (((long long)seqlen + 128) * heads * headdim * esize >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "a (batch, head) slice of seqlen*heads*headdim elements "
+                "must span less than 2^31 bytes");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (wl < -1 || wr < -1)

@@ -46,8 +46,9 @@
  *     else seqlen. A query row with no visible key gets O = 0, LSE = -inf and
  *     zero gradient contributions.
  *   - Supported sizes: headdim in {64, 128}; batch, heads, seqlen >= 1;
- *     batch * heads * seqlen < 2^31 and seqlen <= 2^24; softmax_scale finite
- *     and > 0.
+ *     batch * heads * seqlen < 2^31 and seqlen <= 2^24; one (batch, head)
+ *     slice, (seqlen + 128) * heads * headdim elements, below 2^31 bytes
+ *     (else FA_ERR_UNSUPPORTED); softmax_scale finite and > 0.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

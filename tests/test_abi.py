@@ -61,6 +61,7 @@ def fwd(lib, **kw):
     (dict(N=(1 << 24) + 1), fb.FA_ERR_INVALID_ARG, "seqlen"),
     (dict(B=1 << 16, H=1 << 8, N=1 << 8), fb.FA_ERR_INVALID_ARG, "2^31"),
     (dict(D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
+    (dict(H=64, N=1 << 17, D=128), fb.FA_ERR_UNSUPPORTED, "2^31 bytes"),
     (dict(dtype=7), fb.FA_ERR_UNSUPPORTED, "dtype"),
     (dict(scale=float("nan")), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
     (dict(scale=0.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
