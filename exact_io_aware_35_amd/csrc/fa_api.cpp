@@ -50,9 +50,12 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
     return fail(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (wl < -1 || wr < -1)
     return fail(FA_ERR_INVALID_ARG, "window bounds must be >= -1 (got %d, %d)", wl, wr);
-  *wl_eff = wl;
+  // A bound of seqlen or more excludes no key (0 <= i, j < seqlen), so it is
+  // folded to "unbounded"; kernel index sums such as i + wr + 1 then stay
+  // far below 2^31.
+  *wl_eff = wl >= seqlen ? -1 : wl;
   // causal (j <= i) intersected with j <= i + wr (wr >= 0) is j <= i.
-  *wr_eff = causal ? 0 : wr;
+  *wr_eff = causal ? 0 : (wr >= seqlen ? -1 : wr);
   return FA_OK;
 }
 

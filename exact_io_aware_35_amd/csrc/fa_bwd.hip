@@ -14,53 +14,25 @@
 // Three kernels, no atomics, so the result is deterministic (the flash_attn
 // docstring's deterministic backward, claire-chang.com notes):
 //   bwd_drow_kernel : D_i from O and dO (bandwidth-bound).
-//   bwd_dkdv_kernel : one work-group per key block; each wave keeps dK and dV
-//                     of 32 keys in registers and loops over query tiles.
-//   bwd_dq_kernel   : one work-group per query block; each wave keeps dQ of
-//                     32 queries in registers and loops over key tiles.
-// Products whose operand is P or dS run on fp16 MFMA (P and dS in fp16 carry
-// 3 more mantissa bits than bf16; bf16 inputs convert to fp16 exactly in the
-// normal range); S and dP use bf16 MFMA on the bf16 inputs directly.
+//   bwd_dkdv_kernel : one work-group per key block; each wave keeps K, V, dK
+//                     and dV of 32 keys in registers and streams the query
+//                     tiles (Q, dO, LSE, D) through LDS.
+//   bwd_dq_kernel   : one work-group per query block; each wave keeps Q, dO
+//                     and dQ of 32 queries in registers and streams the key
+//                     tiles (K, V) through LDS.
+// Every product with P or dS as an operand runs on fp16 MFMA: P and dS carry
+// 3 more mantissa bits in fp16 than in bf16, and the bf16 inputs it meets (Q,
+// K, dO) convert to fp16 exactly in fp16's normal range. Tiles are staged in
+// LDS in the swizzled row-major layout of fa_common.h, so the transposed
+// operands (dO^T, Q^T, K^T) come from ds_read_b64_tr_b16 reads and no wave
+// ever transposes data in registers. Accumulation is fp32 throughout.
+
+#include <type_traits>
 
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
-
-// Same permutation as the forward's transposed V: inside each 16-row group,
-// bits 2 and 3 of the row index swap, so the 8 rows one lane feeds to a
-// 32x32x16 MFMA from an accumulator are contiguous.
-__device__ __forceinline__ int tr_pos(int k) {
-  return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
-}
-
-// bf16 pair (one u32) -> two fp16 in one u32.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
-  return pack_f16x2(bf16_lo(u), bf16_hi(u));
-}
-
-// Write `rows` (2 or 4) staged 16-byte chunks (8 bf16 of one row each, rows
-// r0..r0+rows-1, columns 8 dc .. 8 dc + 7) transposed into an fp16 LDS tile
-// T[col][tr_pos(row)] with row stride TSTR.
-template <int ROWS, int TSTR>
-__device__ __forceinline__ void store_transposed_f16(_Float16* T, const u32x4_t* reg, int r0,
-                                                     int dc) {
-  const int pos = tr_pos(r0);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    _Float16* lo = T + (8 * dc + 2 * e) * TSTR + pos;
-    _Float16* hi = lo + TSTR;
-    if constexpr (ROWS == 4) {
-      *(u32x2_t*)lo = u32x2_t{pack_f16x2(bf16_lo(reg[0][e]), bf16_lo(reg[1][e])),
-                              pack_f16x2(bf16_lo(reg[2][e]), bf16_lo(reg[3][e]))};
-      *(u32x2_t*)hi = u32x2_t{pack_f16x2(bf16_hi(reg[0][e]), bf16_hi(reg[1][e])),
-                              pack_f16x2(bf16_hi(reg[2][e]), bf16_hi(reg[3][e]))};
-    } else {
-      *(uint32_t*)lo = pack_f16x2(bf16_lo(reg[0][e]), bf16_lo(reg[1][e]));
-      *(uint32_t*)hi = pack_f16x2(bf16_hi(reg[0][e]), bf16_hi(reg[1][e]));
-    }
-  }
-}
 
 // ---------------------------------------------------------------- D_i
 
@@ -92,154 +64,213 @@ __global__ void __launch_bounds__(256) bwd_drow_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, int NW, int BMQ>
-__global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NT = NW * 64, BNK = NW * 32;
-  constexpr int NSTR = D + 8;             // natural [row][d] bf16 tiles
-  constexpr int TSTR = BMQ + 8;           // transposed [d][row] fp16 tiles
-  constexpr int QPT = BMQ * D / 8 / NT;   // query rows per thread when staging
-  constexpr int QG = BMQ / QPT;
-  static_assert(QPT == 2 || QPT == 4, "staging handles 2 or 4 rows per thread");
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[BMQ * NSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 sdO[BMQ * NSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 sQt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 sdOt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) float sL[BMQ];   // LSE * log2(e), +inf for no row
-  __shared__ __attribute__((aligned(16))) float sDr[BMQ];  // D_i
+template <int D>
+struct KvCfg {
+  static constexpr int NW = 4;                 // waves per work-group, 32 keys each
+  static constexpr int BK = NW * 32;           // keys per work-group
+  static constexpr int BQ = 64;                // query rows per tile
+  static constexpr int NT = NW * 64;
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int TILE = BQ * D * 2;      // bytes of the fp16 Q or dO tile
+  static constexpr int CH = BQ * CPR / NT;     // chunks each thread stages per matrix
+  static constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // one buffer: Q | dO | LSE2 | D
+  static constexpr int DS = D / 16, DB = D / 32, QS = BQ / 32, KS = BQ / 16;
+  static_assert(CH >= 1 && BQ * CPR % NT == 0, "tile must split evenly over the threads");
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// dK and dV of a block of NW * 32 keys. Per query tile and wave (32 keys):
+//   S = Q K^T and dP = dO V^T       (A: Q / dO rows from LDS, B: K / V registers;
+//                                    each lane then holds one key's column),
+//   P = 2^(c2 S - LSE2), dS = P (dP - D)   (LSE2 = LSE log2 e, +inf for empty rows),
+//   dV^T += dO^T P and dK^T += Q^T dS     (A: transposed LDS reads, B: P / dS
+//                                    packed to fp16 straight from the accumulators).
+// Query tiles are double-buffered: the next tile's global loads are in flight
+// in registers while the current one is computed, then converted to fp16 and
+// written to the other buffer before the one barrier per tile.
+template <int D>
+__global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
+  using C = KvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hf = lane >> 5;
   int bh, kblk;
   map_block(p.B * p.H, p.nblk, p.xcd_groups, 0, bh, kblk);
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
-  const size_t rs = (size_t)p.H * D;
+  const int rs = p.H * D;
   const size_t base = ((size_t)b * N * p.H + h) * D;
-  const __bf16* Q = (const __bf16*)p.q + base;
-  const __bf16* K = (const __bf16*)p.k + base;
-  const __bf16* V = (const __bf16*)p.v + base;
-  const __bf16* dO = (const __bf16*)p.dout + base;
   const float* LSE = p.lse + ((size_t)b * p.H + h) * N;
   const float* DR = p.drow + ((size_t)b * p.H + h) * N;
 
-  const int k0 = kblk * BNK;
-  const int key = k0 + wave * 32 + ln;  // this lane's key
-  bf16x8_t kf[D / 16], vf[D / 16];
+  // This lane's key, and its K and V rows as fp16 B operands:
+  // kf[s] = K[key][16 s + 8 hf .. +8). Keys past N are clamped (and masked).
+  const int k0 = kblk * C::BK, wk0 = k0 + wave * 32, wk1 = wk0 + 31;
+  const int key = wk0 + ln;
+  f16x8_t kf[C::DS], vf[C::DS];
+  {
+    const size_t off = base + (size_t)min(key, N - 1) * rs + 8 * hf;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (key < N) {
-      kf[s] = ld_global<bf16x8_t>(K + (size_t)key * rs + 16 * s + 8 * hf);
-      vf[s] = ld_global<bf16x8_t>(V + (size_t)key * rs + 16 * s + 8 * hf);
-    } else {
-      kf[s] = bf16x8_t{};
-      vf[s] = bf16x8_t{};
+    for (int s = 0; s < C::DS; ++s) {
+      kf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.k + off + 16 * s)));
+      vf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + off + 16 * s)));
     }
   }
-  f32x16_t dk[D / 32], dv[D / 32];
+
+  // Queries that see a key of the work-group / of this wave: [lo, hi).
+  int qlo = 0, qhi = 0, wqlo = 0, wqhi = 0;
+  {
+    const int klast = min(k0 + C::BK, kl) - 1;
+    if (k0 <= klast) {
+      qlo = p.mask.wr >= 0 ? max(0, k0 - p.mask.wr) : 0;
+      qhi = p.mask.wl >= 0 ? min(N, klast + p.mask.wl + 1) : N;
+    }
+    const int wklast = min(wk1, kl - 1);
+    if (wk0 <= wklast) {
+      wqlo = p.mask.wr >= 0 ? max(0, wk0 - p.mask.wr) : 0;
+      wqhi = p.mask.wl >= 0 ? min(N, wklast + p.mask.wl + 1) : N;
+    }
+  }
+  const int t0 = qlo / C::BQ, t1 = qhi > qlo ? (qhi + C::BQ - 1) / C::BQ : t0;
+  // Rows i that see this lane's key j: vqlo <= i <= vqhi (empty for j >= kl).
+  const int vqlo = key >= kl ? INT_MAX : (p.mask.wr >= 0 ? key - p.mask.wr : 0);
+  const int vqhi = p.mask.wl >= 0 ? key + p.mask.wl : INT_MAX;
+
+  // Staging: chunk u = tid + NT j of a tile is (row u / CPR, chunk u % CPR);
+  // rows at or past N read as zero through the buffer range check.
+  const int rs2 = rs * 2;
+  const int nbytes = ((N - 1) * rs + D) * 2;
+  const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc((const __bf16*)p.q + base, nbytes);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc((const __bf16*)p.dout + base, nbytes);
+  int gof[C::CH], lof[C::CH];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) { dk[d] = f32x16_t{}; dv[d] = f32x16_t{}; }
-
-  // Queries that see at least one key of this block (keys >= kl see none).
-  const int klast = min(k0 + BNK, kl) - 1;
-  int qlo = 0, qhi = 0;
-  if (k0 <= klast) {
-    qlo = p.mask.wr >= 0 ? max(0, k0 - p.mask.wr) : 0;
-    qhi = p.mask.wl >= 0 ? min(N, klast + p.mask.wl + 1) : N;
+  for (int j = 0; j < C::CH; ++j) {
+    const int u = tid + C::NT * j, row = u / C::CPR, c = u % C::CPR;
+    gof[j] = row * rs2 + c * 16;
+    lof[j] = tile_chunk_off<D>(row, c);
   }
-  const int t0 = qlo / BMQ, t1 = qhi > qlo ? (qhi + BMQ - 1) / BMQ : t0;
-  const int wk0 = k0 + wave * 32, wk1 = wk0 + 31;
-  const int wklast = min(wk1, kl - 1);
-  int wqlo = 0, wqhi = 0;
-  if (wk0 <= wklast) {
-    wqlo = p.mask.wr >= 0 ? max(0, wk0 - p.mask.wr) : 0;
-    wqhi = p.mask.wl >= 0 ? min(N, wklast + p.mask.wl + 1) : N;
-  }
-
-  u32x4_t qreg[QPT], oreg[QPT];
-  float lreg = INFINITY, dreg = 0.f;
-  const int sg = tid % QG, sdc = tid / QG;
+  u32x4_t qst[C::CH], ost[C::CH];
+  float lst = INFINITY, dst = 0.f;
   auto load_tile = [&](int t) {
-    const int qb = t * BMQ;
+    const int soff = t * C::BQ * rs2;
 #pragma unroll
-    for (int r = 0; r < QPT; ++r) {
-      const int row = qb + sg * QPT + r;
-      qreg[r] = row < N ? ld_global<u32x4_t>(Q + (size_t)row * rs + 8 * sdc) : u32x4_t{};
-      oreg[r] = row < N ? ld_global<u32x4_t>(dO + (size_t)row * rs + 8 * sdc) : u32x4_t{};
+    for (int j = 0; j < C::CH; ++j) {
+      qst[j] = buffer_load16(qrsrc, gof[j], soff);
+      ost[j] = buffer_load16(orsrc, gof[j], soff);
     }
-    if (tid < BMQ) {
-      const int row = qb + tid;
-      const float L = row < N ? LSE[row] : -INFINITY;
-      lreg = L == -INFINITY ? INFINITY : L * 1.4426950408889634f;
-      dreg = row < N ? DR[row] : 0.f;
+    if (wave == 0) {
+      const int row = t * C::BQ + lane;
+      const float L = LSE[min(row, N - 1)], Dv = DR[min(row, N - 1)];
+      lst = (row >= N || L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;
+      dst = row >= N ? 0.f : Dv;
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    char* sb = smem + buf * C::BUF;
 #pragma unroll
-    for (int r = 0; r < QPT; ++r) {
-      *(u32x4_t*)&sQ[(sg * QPT + r) * NSTR + 8 * sdc] = qreg[r];
-      *(u32x4_t*)&sdO[(sg * QPT + r) * NSTR + 8 * sdc] = oreg[r];
+    for (int j = 0; j < C::CH; ++j) {
+      *(u32x4_t*)(sb + lof[j]) = bf16x8_to_f16x8(qst[j]);
+      *(u32x4_t*)(sb + C::TILE + lof[j]) = bf16x8_to_f16x8(ost[j]);
     }
-    store_transposed_f16<QPT, TSTR>(sQt, qreg, sg * QPT, sdc);
-    store_transposed_f16<QPT, TSTR>(sdOt, oreg, sg * QPT, sdc);
-    if (tid < BMQ) {
-      sL[tid] = lreg;
-      sDr[tid] = dreg;
+    if (wave == 0) {
+      ((float*)(sb + 2 * C::TILE))[lane] = lst;
+      ((float*)(sb + 2 * C::TILE))[C::BQ + lane] = dst;
     }
   };
 
-  if (t0 < t1) load_tile(t0);
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();  // the previous tile's readers are done
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t1) load_tile(t + 1);
-    const int qb = t * BMQ;
-    if (qb < wqhi && qb + BMQ > wqlo) {
-      const bool full = block_all_visible(p.mask, kl, qb, min(qb + BMQ, N) - 1, wk0, wk1);
-      u32x4_t ppk[BMQ / 16], dpk[BMQ / 16];  // fp16 P and dS, 8 queries per operand
+  // Operand offsets within a tile: row operand of d-step s is row ln, chunk
+  // 2 s + hf; transposed operands as tile_tr_off. Both stay valid when a
+  // multiple of 16 rows is added (the swizzle only sees the low 4 row bits).
+  int roff[C::DS];
 #pragma unroll
-      for (int qs = 0; qs < BMQ / 32; ++qs) {
-        // S = Q K^T and dP = dO V^T for 32 queries x this lane's key.
-        f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+  for (int s = 0; s < C::DS; ++s) roff[s] = tile_chunk_off<D>(ln, 2 * s + hf);
+  int troff[C::DB][2];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const int off = (32 * qs + ln) * NSTR + 16 * s + 8 * hf;
-          sa = mfma_bf16(*(const bf16x8_t*)&sQ[off], kf[s], sa);
-          pa = mfma_bf16(*(const bf16x8_t*)&sdO[off], vf[s], pa);
-        }
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          float pv[2], dsv[2];
+    for (int t = 0; t < 2; ++t) troff[db][t] = tile_tr_off<D>(lane, db, t);
+
+  f32x16_t dk[C::DB], dv[C::DB];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int ql = 32 * qs + 8 * ((i + u) >> 2) + 4 * hf + ((i + u) & 3);
-            float pp = exp2_fast(fmaf(sa[i + u], p.scale_log2, -sL[ql]));
-            if (!full && !visible(p.mask, kl, qb + ql, key)) pp = 0.f;
-            pv[u] = pp;
-            dsv[u] = pp * (pa[i + u] - sDr[ql]);
-          }
-          ppk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(pv[0], pv[1]);
-          dpk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(dsv[0], dsv[1]);
+  for (int d = 0; d < C::DB; ++d) { dk[d] = f32x16_t{}; dv[d] = f32x16_t{}; }
+
+  auto compute = [&](int t, int buf) {
+    const int qb = t * C::BQ;
+    if (!(qb < wqhi && qb + C::BQ > wqlo)) return;  // wave-uniform
+    const char* sq = smem + buf * C::BUF;
+    const char* so = sq + C::TILE;
+    const float* sl = (const float*)(sq + 2 * C::TILE);
+    const float* sd = sl + C::BQ;
+    const bool full = block_all_visible(p.mask, kl, qb, min(qb + C::BQ, N) - 1, wk0, wk1);
+    u32x4_t pk[C::KS], dsk[C::KS];
+#pragma unroll
+    for (int qs = 0; qs < C::QS; ++qs) {
+      f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        const int off = qs * 32 * C::CPR * 16 + roff[s];
+        sa = mfma_f16(*(const f16x8_t*)(sq + off), kf[s], sa);
+        pa = mfma_f16(*(const f16x8_t*)(so + off), vf[s], pa);
+      }
+      // Element i of a lane is query row 8 (i / 4) + 4 hf + i % 4 of the block.
+      f32x4_t l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[g] = *(const f32x4_t*)(sl + 32 * qs + 8 * g + 4 * hf);
+        d4[g] = *(const f32x4_t*)(sd + 32 * qs + 8 * g + 4 * hf);
+      }
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = qb + 32 * qs + 8 * (i >> 2) + 4 * hf + (i & 3);
+          sa[i] = (row >= vqlo) & (row <= vqhi) ? sa[i] : -INFINITY;
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (fp16 operands, fp32 accumulation).
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-        for (int ks = 0; ks < BMQ / 16; ++ks) {
-          const int off = (32 * d + ln) * TSTR + 16 * ks + 8 * hf;
-          dv[d] = mfma_f16(*(const f16x8_t*)&sdOt[off], __builtin_bit_cast(f16x8_t, ppk[ks]), dv[d]);
-          dk[d] = mfma_f16(*(const f16x8_t*)&sQt[off], __builtin_bit_cast(f16x8_t, dpk[ks]), dk[d]);
-        }
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
+        const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -l4[i >> 2][(i & 3) + 1]));
+        const float s0 = p0 * (pa[i] - d4[i >> 2][i & 3]);
+        const float s1 = p1 * (pa[i + 1] - d4[i >> 2][(i & 3) + 1]);
+        pk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
+        dsk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(s0, s1);
+      }
     }
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int ro = ks * 16 * C::CPR * 16;
+        const u32x2_t o0 = lds_read_tr16(so + ro + troff[d][0]), o1 = lds_read_tr16(so + ro + troff[d][1]);
+        const u32x2_t q0 = lds_read_tr16(sq + ro + troff[d][0]), q1 = lds_read_tr16(sq + ro + troff[d][1]);
+        dv[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{o0[0], o0[1], o1[0], o1[1]}),
+                         __builtin_bit_cast(f16x8_t, pk[ks]), dv[d]);
+        dk[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]}),
+                         __builtin_bit_cast(f16x8_t, dsk[ks]), dk[d]);
+      }
+  };
+
+  if (t0 < t1) {
+    load_tile(t0);
+    store_tile(0);
+    __syncthreads();
+  }
+  for (int t = t0; t < t1; ++t) {
+    const int cur = (t - t0) & 1;
+    if (t + 1 < t1) load_tile(t + 1);
+    compute(t, cur);
+    if (t + 1 < t1) store_tile(cur ^ 1);
+    __syncthreads();
   }
 
+  // Lane holds dK^T / dV^T rows (d) 32 d + 8 g + 4 hf + (0..3) of its key.
   if (key < N) {
     __bf16* dkrow = (__bf16*)p.dk + base + (size_t)key * rs;
     __bf16* dvrow = (__bf16*)p.dv + base + (size_t)key * rs;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+    for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
@@ -254,130 +285,193 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, int NW, int BN>
-__global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(BwdParams p) {
-  constexpr int NT = NW * 64, BM = NW * 32;
-  constexpr int NSTR = D + 8;
-  constexpr int TSTR = BN + 8;
-  constexpr int KPT = BN * D / 8 / NT;
-  constexpr int KG = BN / KPT;
-  static_assert(KPT == 2 || KPT == 4, "staging handles 2 or 4 rows per thread");
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BN * NSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[BN * NSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 sKt[D * TSTR];
+template <int D>
+struct DqCfg {
+  static constexpr int NW = D == 128 ? 8 : 4;  // waves per work-group, 32 queries each
+  static constexpr int BM = NW * 32;           // query rows per work-group
+  static constexpr int BN = 64;                // keys per tile
+  static constexpr int NT = NW * 64;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BN * D * 2;      // bytes of one K (fp16) or V (bf16) tile
+  static constexpr int CH = BN * CPR / NT;     // K chunks each thread stages
+  static constexpr int LPW = TILE / 1024 / NW; // V: 1 KiB direct-to-LDS loads per wave
+  static constexpr int DS = D / 16, DB = D / 32, KB = BN / 32, KS = BN / 16;
+  static_assert(CH >= 1 && BN * CPR % NT == 0, "K tile must split evenly over the threads");
+  static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "V tile must split into 1 KiB loads");
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// dQ of a block of NW * 32 queries, in the forward's orientation: per key
+// tile and wave,
+//   S^T = K Q^T and dP^T = V dO^T      (A: K / V rows from LDS, B: Q / dO
+//                                       registers; each lane holds one query),
+//   P = 2^(c2 S - LSE2), dS^T = P (dP^T - D),
+//   dQ^T += K^T dS^T                    (A: transposed K reads; B: dS^T packed
+//                                       to fp16 from the accumulators).
+// K is staged through registers (converted to fp16 for the dS product), V is
+// copied global -> LDS directly (its products stay bf16); both are
+// double-buffered with one barrier per tile.
+template <int D>
+__global__ void __launch_bounds__(DqCfg<D>::NT) bwd_dq_kernel(BwdParams p) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];  // [buf][K | V]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hf = lane >> 5;
   int bh, qblk;
   map_block(p.B * p.H, p.nblk, p.xcd_groups, p.mask.wr >= 0, bh, qblk);
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
-  const size_t rs = (size_t)p.H * D;
+  const int rs = p.H * D;
   const size_t base = ((size_t)b * N * p.H + h) * D;
-  const __bf16* Q = (const __bf16*)p.q + base;
-  const __bf16* K = (const __bf16*)p.k + base;
-  const __bf16* V = (const __bf16*)p.v + base;
-  const __bf16* dO = (const __bf16*)p.dout + base;
 
-  const int q0 = qblk * BM;
-  const int qi = q0 + wave * 32 + ln;
-  bf16x8_t qf[D / 16], of[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (qi < N) {
-      qf[s] = ld_global<bf16x8_t>(Q + (size_t)qi * rs + 16 * s + 8 * hf);
-      of[s] = ld_global<bf16x8_t>(dO + (size_t)qi * rs + 16 * s + 8 * hf);
-    } else {
-      qf[s] = bf16x8_t{};
-      of[s] = bf16x8_t{};
-    }
-  }
-  float lse2 = INFINITY, dr = 0.f;
-  if (qi < N) {
-    const float L = p.lse[((size_t)b * p.H + h) * N + qi];
-    lse2 = L == -INFINITY ? INFINITY : L * 1.4426950408889634f;
-    dr = p.drow[((size_t)b * p.H + h) * N + qi];
-  }
-  f32x16_t dq[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) dq[d] = f32x16_t{};
-
+  const int q0 = qblk * C::BM, wq0 = q0 + wave * 32;
   int klo, khi;
-  key_range(p.mask, kl, q0, min(q0 + BM, N) - 1, klo, khi);
-  const int t0 = klo / BN, t1 = (khi + BN - 1) / BN;
-  const int wq0 = q0 + wave * 32, wq1 = min(wq0 + 31, N - 1);
+  key_range(p.mask, kl, q0, min(q0 + C::BM, N) - 1, klo, khi);
+  const int t0 = klo / C::BN, t1 = (khi + C::BN - 1) / C::BN;
+  const int wq1 = min(wq0 + 31, N - 1);
   int wklo = 0, wkhi = 0;
   if (wq0 <= wq1) key_range(p.mask, kl, wq0, wq1, wklo, wkhi);
 
-  u32x4_t kreg[KPT], vreg[KPT];
-  const int sg = tid % KG, sdc = tid / KG;
-  auto load_tile = [&](int t) {
-    const int kt = t * BN;
+  // This lane's query row: Q (fp16) and dO (bf16) as B operands, LSE2 and D.
+  const int qi = wq0 + ln, qrow = min(qi, N - 1);
+  f16x8_t qf[C::DS];
+  bf16x8_t of[C::DS];
+  {
+    const size_t off = base + (size_t)qrow * rs + 8 * hf;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int row = kt + sg * KPT + r;
-      kreg[r] = row < N ? ld_global<u32x4_t>(K + (size_t)row * rs + 8 * sdc) : u32x4_t{};
-      vreg[r] = row < N ? ld_global<u32x4_t>(V + (size_t)row * rs + 8 * sdc) : u32x4_t{};
+    for (int s = 0; s < C::DS; ++s) {
+      qf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.q + off + 16 * s)));
+      of[s] = ld_global<bf16x8_t>((const __bf16*)p.dout + off + 16 * s);
     }
+  }
+  float lse2, dr;
+  {
+    const size_t r = ((size_t)b * p.H + h) * N + qrow;
+    const float L = p.lse[r];
+    lse2 = (qi >= N || L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;
+    dr = p.drow[r];
+  }
+
+  const int rs2 = rs * 2;
+  const int nbytes = ((N - 1) * rs + D) * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const __bf16*)p.k + base, nbytes);
+  const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc((const __bf16*)p.v + base, nbytes);
+  // K staging (as in the dK/dV kernel) and V direct loads (as in the forward:
+  // load j of this wave fills LDS chunks [(wave * LPW + j) * 64, +64), and the
+  // swizzle is applied to the global chunk each lane fetches).
+  int gof[C::CH], lof[C::CH], loff[C::LPW];
+#pragma unroll
+  for (int j = 0; j < C::CH; ++j) {
+    const int u = tid + C::NT * j, row = u / C::CPR, c = u % C::CPR;
+    gof[j] = row * rs2 + c * 16;
+    lof[j] = tile_chunk_off<D>(row, c);
+  }
+#pragma unroll
+  for (int j = 0; j < C::LPW; ++j) {
+    const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
+    loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
+  }
+  u32x4_t kst[C::CH];
+  auto load_tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int soff = t * C::BN * rs2;
+#pragma unroll
+    for (int j = 0; j < C::CH; ++j) kst[j] = buffer_load16(krsrc, gof[j], soff);
+    char* vd = smem + (2 * buf + 1) * C::TILE + wave * C::LPW * 1024;
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) buffer_load_lds16(vrsrc, vd + j * 1024, loff[j], soff);
   };
-  auto store_tile = [&]() {
+  auto store_k = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    char* kd = smem + (2 * buf) * C::TILE;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      *(u32x4_t*)&sK[(sg * KPT + r) * NSTR + 8 * sdc] = kreg[r];
-      *(u32x4_t*)&sV[(sg * KPT + r) * NSTR + 8 * sdc] = vreg[r];
-    }
-    store_transposed_f16<KPT, TSTR>(sKt, kreg, sg * KPT, sdc);
+    for (int j = 0; j < C::CH; ++j) *(u32x4_t*)(kd + lof[j]) = bf16x8_to_f16x8(kst[j]);
   };
 
-  if (t0 < t1) load_tile(t0);
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t1) load_tile(t + 1);
-    const int kt = t * BN;
-    if (kt < wkhi && kt + BN > wklo) {
-      const bool full = block_all_visible(p.mask, kl, wq0, wq1, kt, kt + BN - 1);
-      u32x4_t dsk[BN / 16];
+  int roff[C::DS];
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T: 32 keys x this lane's query.
-        f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+  for (int s = 0; s < C::DS; ++s) roff[s] = tile_chunk_off<D>(ln, 2 * s + hf);
+  int troff[C::DB][2];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const int off = (32 * kb + ln) * NSTR + 16 * s + 8 * hf;
-          sa = mfma_bf16(*(const bf16x8_t*)&sK[off], qf[s], sa);
-          pa = mfma_bf16(*(const bf16x8_t*)&sV[off], of[s], pa);
-        }
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          float dsv[2];
+    for (int t = 0; t < 2; ++t) troff[db][t] = tile_tr_off<D>(lane, db, t);
+
+  f32x16_t dq[C::DB];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int j = kt + 32 * kb + 8 * ((i + u) >> 2) + 4 * hf + ((i + u) & 3);
-            float pp = exp2_fast(fmaf(sa[i + u], p.scale_log2, -lse2));
-            if (!full && !visible(p.mask, kl, qi, j)) pp = 0.f;
-            dsv[u] = pp * (pa[i + u] - dr);
-          }
-          dsk[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_f16x2(dsv[0], dsv[1]);
+  for (int d = 0; d < C::DB; ++d) dq[d] = f32x16_t{};
+
+  auto compute = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const char* sk = smem + (2 * buf) * C::TILE;
+    const char* sv = sk + C::TILE;
+    const int kt = t * C::BN;
+    if (!(kt < wkhi && kt + C::BN > wklo)) return;  // wave-uniform
+    const bool full = block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1);
+    u32x4_t dsk[C::KS];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        const int off = kb * 32 * C::CPR * 16 + roff[s];
+        sa = mfma_f16(*(const f16x8_t*)(sk + off), qf[s], sa);
+        pa = mfma_bf16(*(const bf16x8_t*)(sv + off), of[s], pa);
+      }
+      if (!full) {
+        int lo, hi;
+        visible_span(p.mask, kl, qi, lo, hi);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = kt + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          sa[i] = (j >= lo) & (j <= hi) ? sa[i] : -INFINITY;
         }
       }
-      // dQ^T += K^T dS^T.
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d)
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -lse2));
+        const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -lse2));
+        dsk[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0 * (pa[i] - dr), p1 * (pa[i + 1] - dr));
+      }
+    }
 #pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks) {
-          const int off = (32 * d + ln) * TSTR + 16 * ks + 8 * hf;
-          dq[d] = mfma_f16(*(const f16x8_t*)&sKt[off], __builtin_bit_cast(f16x8_t, dsk[ks]), dq[d]);
-        }
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int ro = ks * 16 * C::CPR * 16;
+        const u32x2_t k0 = lds_read_tr16(sk + ro + troff[d][0]), k1 = lds_read_tr16(sk + ro + troff[d][1]);
+        dq[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{k0[0], k0[1], k1[0], k1[1]}),
+                         __builtin_bit_cast(f16x8_t, dsk[ks]), dq[d]);
+      }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // Key tiles alternate between two LDS buffers (tile t0 + i in buffer i % 2).
+  auto interval = [&](int t, auto cur, auto nxt) {
+    if (t + 1 < t1) load_tile(t + 1, nxt);
+    compute(t, cur);
+    if (t + 1 < t1) store_k(nxt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  if (t0 < t1) {
+    load_tile(t0, B0{});
+    store_k(B0{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = t0; t < t1; t += 2) {
+      interval(t, B0{}, B1{});
+      if (t + 1 < t1) interval(t + 1, B1{}, B0{});
     }
   }
 
   if (qi < N) {
     __bf16* row = (__bf16*)p.dq + base + (size_t)qi * rs;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+    for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
@@ -390,20 +484,16 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- launcher
 
-static constexpr int kBwdWaves = 4;
-static constexpr int kBwdTile = 64;
-
 template <int D>
 static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
-  constexpr int NT = kBwdWaves * 64, BLK = kBwdWaves * 32;
   const long long rows = (long long)p.B * p.N * p.H;
   const long long rpb = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_drow_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
                      stream, p);
-  p.nblk = (p.N + BLK - 1) / BLK;
-  const dim3 grid(p.B * p.H * p.nblk);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, kBwdWaves, kBwdTile>), grid, dim3(NT), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, kBwdTile>), grid, dim3(NT), 0, stream, p);
+  p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(KvCfg<D>::NT), 0, stream, p);
+  p.nblk = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NT), 0, stream, p);
   return hipGetLastError();
 }
 

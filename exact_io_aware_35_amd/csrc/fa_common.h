@@ -122,7 +122,9 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
 }
 
-// Raw buffer descriptor over [base, base + bytes): loads past the end return 0.
+// Raw buffer descriptor over [base, base + bytes): loads past the end return 0
+// (the range check covers voffset + soffset, so a tile's first row may go in
+// the scalar offset).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
@@ -135,7 +137,53 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
                                            voffset, soffset, 0, 0);
 }
 
+// 16-byte buffer load into registers (zero past the descriptor's end).
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
+}
+
 template <typename T>
 __device__ __forceinline__ T ld_global(const void* p) { return *reinterpret_cast<const T*>(p); }
+
+// 8 bf16 (one 16-byte chunk) -> 8 fp16, rounded to nearest even (exact for
+// magnitudes in fp16's normal range).
+__device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t u) {
+  u32x4_t r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_f16x2(bf16_lo(u[e]), bf16_hi(u[e]));
+  return r;
+}
+
+// LDS tiles of 16-bit values, [rows][D] row-major, with the 16-byte chunks of
+// each row XOR-swizzled: chunk c of row r is stored at position c ^ lds_swz(r).
+// With it the two read patterns of the kernels are free of bank conflicts:
+// 16 consecutive rows reading one chunk (a row-major MFMA operand) and 4
+// consecutive rows x 4 consecutive chunks (a transposed read). lds_swz only
+// depends on the low 4 bits of the row.
+template <int D>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset of chunk c (elements 8c .. 8c+7) of row r in such a tile.
+template <int D>
+__device__ __forceinline__ int tile_chunk_off(int r, int c) {
+  return (r * (D / 8) + (c ^ lds_swz<D>(r))) * 16;
+}
+
+// Byte offset a lane passes to lds_read_tr16 to fetch its half t (t = 0, 1)
+// of a transposed 32x32x16 MFMA operand covering columns 32 db .. 32 db + 31
+// and rows 0..15 of the tile: lane r of 16-lane group g addresses row
+// 8 t + 4 (g / 2) + r / 4 at column 32 db + 16 (g % 2) + 4 (r % 4). Lane l
+// then holds column 32 db + l % 32 at the 8 rows 8 (j / 4) + 4 (l / 32) + j % 4,
+// the row order in which a 32x32 accumulator holds its rows.
+template <int D>
+__device__ __forceinline__ int tile_tr_off(int lane, int db, int t) {
+  const int g = lane >> 4, r = lane & 15;
+  const int row = 8 * t + 4 * (g >> 1) + (r >> 2);
+  const int col = 32 * db + 16 * (g & 1) + 4 * (r & 3);
+  return tile_chunk_off<D>(row, col >> 3) + ((col >> 2) & 1) * 8;
+}
 
 }  // namespace fa

@@ -30,17 +30,6 @@
 
 namespace fa {
 
-// XOR swizzle of the 16-byte chunks of a K or V row in LDS. Chunk c of row r
-// is stored at position c ^ swz(r). With it, the two LDS read patterns of the
-// kernel are free of bank conflicts: 16 consecutive rows reading one chunk
-// (K as an MFMA operand) and 4 consecutive rows x 4 consecutive chunks (V
-// read transposed). swz only depends on the low 4 bits of the row.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
 // Tile shape per head dimension, chosen by measurement on MI355X: at D = 128
 // eight waves share each K/V tile (256 query rows per work-group); at D = 64
 // two independent 4-wave work-groups per CU do better (their barriers do not
@@ -129,7 +118,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
   for (int j = 0; j < C::LPW; ++j) {
     const int u = (wave * C::LPW + j) * 64 + lane;
     const int row = u / C::CPR, pos = u % C::CPR;
-    loff[j] = row * rs2 + (pos ^ swz<D>(row)) * 16;
+    loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
   }
   auto issue_tile = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -143,25 +132,16 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     }
   };
 
-  // LDS read offsets (bytes within a tile). K operand for d-step s: row ln
-  // (+32 kb), logical chunk 2 s + hf. V^T operand for (d-block db, half t of
-  // the 16-key step): lane r of 16-lane group g addresses key row
-  // 8 t + 4 (g / 2) + r / 4 (+16 ks) at d = 32 db + 16 (g % 2) + 4 (r % 4).
+  // LDS read offsets (bytes within a tile): the K operand for d-step s is
+  // row ln (+32 kb), chunk 2 s + hf; the V^T operand is a transposed read.
   int koff[C::DS];
 #pragma unroll
-  for (int s = 0; s < C::DS; ++s) koff[s] = (ln * C::CPR + ((2 * s + hf) ^ swz<D>(ln))) * 16;
+  for (int s = 0; s < C::DS; ++s) koff[s] = tile_chunk_off<D>(ln, 2 * s + hf);
   int voff[C::DB][2];
-  {
-    const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = 8 * t + 4 * (g >> 1) + (r >> 2);
-        const int col = 32 * db + 16 * (g & 1) + 4 * (r & 3);
-        voff[db][t] = (row * C::CPR + ((col >> 3) ^ swz<D>(row))) * 16 + ((col >> 2) & 1) * 8;
-      }
-  }
+    for (int t = 0; t < 2; ++t) voff[db][t] = tile_tr_off<D>(lane, db, t);
 
   f32x16_t oacc[C::DB][C::QB];
 #pragma unroll

@@ -215,6 +215,37 @@ def test_backward_lengths(N):
     check_backward(d)
 
 
+@pytest.mark.parametrize("mask", [dict(), dict(causal=True), dict(causal=True, window=(300, 0)),
+                                  dict(window=(90, 400))],
+                         ids=["none", "causal", "causal-window300", "window90-400"])
+def test_backward_d128_several_blocks(mask):
+    # 1000 keys: 8 key blocks of 128 (the last ragged) and 4 query blocks.
+    d = make_case(1, 1000, 2, 128, dtype="bf16", seed=15, backward=True)
+    check_backward(d, **mask)
+
+
+def test_backward_d128_key_padding():
+    d = make_case(2, 700, 2, 128, dtype="bf16", seed=16, backward=True, seqlens_k=[650, 129])
+    check_backward(d, causal=True)
+    check_backward(d)
+
+
+def test_window_at_or_past_seqlen_is_unbounded():
+    # A window bound >= seqlen excludes nothing; the library treats it as -1.
+    d = make_case(1, 200, 2, 64, dtype="bf16", seed=17, backward=True)
+    q, k, v, do = dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["dout"])
+    big = 2 ** 31 - 1
+    ref_o, ref_lse = forward(q, k, v)
+    ref_g = backward(q, k, v, ref_o, ref_lse, do)
+    for window in [(big, big), (200, 200), (200, -1), (-1, big)]:
+        o, lse = forward(q, k, v, window=window)
+        g = backward(q, k, v, o, lse, do, window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse), window
+        for a, b in zip(g, ref_g):
+            assert torch.equal(a, b), window
+
+
 def test_backward_is_deterministic_and_writes_everything():
     d = make_case(2, 300, 2, 64, dtype="bf16", seed=14, backward=True)
     q, k, v, do = dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["dout"])
@@ -278,6 +309,27 @@ def test_workload_fwd_bwd_full(name, seed):
     check_forward(d, w.dtype, w.causal, w.window, w.softmax_scale)
     errs = check_backward(d, w.causal, w.window, w.softmax_scale)
     print(name, seed, {k: f"{v:.4g}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_b2h8n4096d128_sampled_heads(causal):
+    # Full-size backward in the launch configuration the benchmark times; the
+    # oracle checks every gradient of two (batch, head) slices.
+    w = WORKLOADS["fwd_bf16_b2h8n4096d128"]
+    d = make_inputs(w, 0)
+    g = torch.Generator().manual_seed(5)
+    d["dout"] = torch.randn(d["q"].shape, generator=g).to(torch.bfloat16)
+    q, k, v, do = dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["dout"])
+    o, lse = forward(q, k, v, causal=causal, softmax_scale=w.softmax_scale)
+    grads = [t.cpu() for t in backward(q, k, v, o, lse, do, causal=causal,
+                                       softmax_scale=w.softmax_scale)]
+    for b, h in [(0, 0), (1, 7)]:
+        sl = lambda t: np64(t[b:b + 1, :, h:h + 1, :])
+        ref = attention_backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["dout"]),
+                                 w.softmax_scale, causal, (-1, -1), None)
+        for name, got, want in zip(("dQ", "dK", "dV"), grads, ref):
+            assert_close(got[b:b + 1, :, h:h + 1, :], want, TOL["bf16"]["grad"],
+                         f"{name}[b={b},h={h}]")
 
 
 @pytest.mark.parametrize("name", ["fwd_bf16_b1h16n65536d128_causal",
