@@ -25,10 +25,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall",
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc", "-munsafe-fp-atomics"]
-# Per-source extras. The forward keeps MFMA results in arch VGPRs: it reads
-# every score accumulator with VALU ops, and the accumulator-register form
-# would add a copy per element.
-EXTRA = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extras. MFMA results go to arch VGPRs: the kernels read every
+# score accumulator with VALU ops, and the accumulator-register form would add
+# a copy per element. The long-lived dK/dV accumulators of the backward are
+# pinned to AGPRs by hand (fa_common.h, mfma_f16_agpr).
+EXTRA = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

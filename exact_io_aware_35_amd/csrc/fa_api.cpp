@@ -65,9 +65,23 @@ fa_status_t check_ptr(const void* p, const char* name) {
   return FA_OK;
 }
 
-size_t drow_bytes(int batch, int heads, int seqlen) {
-  size_t n = (size_t)batch * heads * seqlen * sizeof(float);
-  return (n + 255) & ~(size_t)255;
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Backward workspace: the row statistics (2 floats per row), then fp16
+// copies of Q, K and dO; each part starts on a 256-byte boundary.
+struct BwdWorkspace {
+  size_t stats, q16, k16, do16, total;
+};
+BwdWorkspace bwd_workspace(int batch, int heads, int seqlen, int headdim) {
+  const size_t rows = (size_t)batch * heads * seqlen;
+  const size_t half = round256(rows * headdim * 2);
+  BwdWorkspace w;
+  w.stats = 0;
+  w.q16 = round256(rows * 2 * sizeof(float));
+  w.k16 = w.q16 + half;
+  w.do16 = w.k16 + half;
+  w.total = w.do16 + half;
+  return w;
 }
 
 }  // namespace
@@ -130,7 +144,7 @@ size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
   fa_status_t s = check_common(batch, heads, seqlen, headdim, 1.f, 0, -1, -1, dtype, &wl, &wr);
   memcpy(g_msg, saved, sizeof g_msg);
   if (s != FA_OK) return 0;
-  return drow_bytes(batch, heads, seqlen);
+  return bwd_workspace(batch, heads, seqlen, headdim).total;
 }
 
 fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* out,
@@ -152,7 +166,8 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
     if ((s = check_ptr(ptrs[i], names[i])) != FA_OK) return s;
   if (seqlens_k != nullptr && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
-  const size_t need = drow_bytes(batch, heads, seqlen);
+  const BwdWorkspace ws = bwd_workspace(batch, heads, seqlen, headdim);
+  const size_t need = ws.total;
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -161,7 +176,11 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
   fa::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = out; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
-  p.drow = static_cast<float*>(workspace);
+  char* wsb = static_cast<char*>(workspace);
+  p.stats = reinterpret_cast<float*>(wsb + ws.stats);
+  p.q16 = wsb + ws.q16;
+  p.k16 = wsb + ws.k16;
+  p.do16 = wsb + ws.do16;
   p.mask.seqlens_k = seqlens_k;
   p.mask.wl = wl;
   p.mask.wr = wr;

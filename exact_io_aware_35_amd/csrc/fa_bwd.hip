@@ -13,19 +13,22 @@
 //
 // Three kernels, no atomics, so the result is deterministic (the flash_attn
 // docstring's deterministic backward, claire-chang.com notes):
-//   bwd_drow_kernel : D_i from O and dO (bandwidth-bound).
+//   bwd_prep_kernel : per row D_i (from O and dO) and LSE log2 e; fp16 copies
+//                     of Q, K and dO (bandwidth-bound, one pass).
 //   bwd_dkdv_kernel : one work-group per key block; each wave keeps K, V, dK
 //                     and dV of 32 keys in registers and streams the query
-//                     tiles (Q, dO, LSE, D) through LDS.
+//                     tiles (Q, dO and the row statistics) through LDS.
 //   bwd_dq_kernel   : one work-group per query block; each wave keeps Q, dO
 //                     and dQ of 32 queries in registers and streams the key
 //                     tiles (K, V) through LDS.
 // Every product with P or dS as an operand runs on fp16 MFMA: P and dS carry
-// 3 more mantissa bits in fp16 than in bf16, and the bf16 inputs it meets (Q,
-// K, dO) convert to fp16 exactly in fp16's normal range. Tiles are staged in
-// LDS in the swizzled row-major layout of fa_common.h, so the transposed
-// operands (dO^T, Q^T, K^T) come from ds_read_b64_tr_b16 reads and no wave
-// ever transposes data in registers. Accumulation is fp32 throughout.
+// 3 more mantissa bits in fp16 than in bf16, and the bf16 inputs they meet
+// (Q, K, dO) convert to fp16 exactly in fp16's normal range. The conversion is
+// done once, by the pre-pass, so every tile is copied global -> LDS by the
+// direct-to-LDS buffer loads (double-buffered, one barrier per tile), in the
+// swizzled row-major layout of fa_common.h; the transposed operands (dO^T,
+// Q^T, K^T) come from ds_read_b64_tr_b16 reads and no wave transposes data in
+// registers. Accumulation is fp32 throughout.
 
 #include <type_traits>
 
@@ -34,10 +37,13 @@
 
 namespace fa {
 
-// ---------------------------------------------------------------- D_i
+// ---------------------------------------------------------------- pre-pass
 
+// One 16-byte chunk of one (b, i, h) row per thread: D_i = sum_d dO O (fp32),
+// the fp16 copies of the Q, K and dO chunks, and per row the statistics pair
+// (LSE log2 e, or +inf for a row with no visible key; D_i).
 template <int D>
-__global__ void __launch_bounds__(256) bwd_drow_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   constexpr int LPR = D / 8;               // lanes per row, 16 bytes each
   constexpr int RPB = 256 / LPR;           // rows per block
   const int tid = threadIdx.x;
@@ -46,11 +52,17 @@ __global__ void __launch_bounds__(256) bwd_drow_kernel(BwdParams p) {
   const long long R = (long long)p.B * p.N * p.H;
   float acc = 0.f;
   if (r < R) {
-    const u32x4_t o = ld_global<u32x4_t>((const __bf16*)p.o + r * D + 8 * c);
-    const u32x4_t g = ld_global<u32x4_t>((const __bf16*)p.dout + r * D + 8 * c);
+    const size_t e = (size_t)r * D + 8 * c;
+    const u32x4_t o = ld_global<u32x4_t>((const __bf16*)p.o + e);
+    const u32x4_t g = ld_global<u32x4_t>((const __bf16*)p.dout + e);
+    const u32x4_t q = ld_global<u32x4_t>((const __bf16*)p.q + e);
+    const u32x4_t k = ld_global<u32x4_t>((const __bf16*)p.k + e);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc += bf16_lo(o[e]) * bf16_lo(g[e]) + bf16_hi(o[e]) * bf16_hi(g[e]);
+    for (int j = 0; j < 4; ++j)
+      acc += bf16_lo(o[j]) * bf16_lo(g[j]) + bf16_hi(o[j]) * bf16_hi(g[j]);
+    *(u32x4_t*)((_Float16*)p.do16 + e) = bf16x8_to_f16x8(g);
+    *(u32x4_t*)((_Float16*)p.q16 + e) = bf16x8_to_f16x8(q);
+    *(u32x4_t*)((_Float16*)p.k16 + e) = bf16x8_to_f16x8(k);
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -58,7 +70,9 @@ __global__ void __launch_bounds__(256) bwd_drow_kernel(BwdParams p) {
     const int h = (int)(r % p.H);
     const long long bi = r / p.H;
     const int i = (int)(bi % p.N), b = (int)(bi / p.N);
-    p.drow[((size_t)b * p.H + h) * p.N + i] = acc;
+    const size_t s = ((size_t)b * p.H + h) * p.N + i;
+    const float L = p.lse[s];
+    *(f32x2_t*)(p.stats + 2 * s) = f32x2_t{L == -INFINITY ? INFINITY : L * 1.4426950408889634f, acc};
   }
 }
 
@@ -69,13 +83,13 @@ struct KvCfg {
   static constexpr int NW = 4;                 // waves per work-group, 32 keys each
   static constexpr int BK = NW * 32;           // keys per work-group
   static constexpr int BQ = 64;                // query rows per tile
-  static constexpr int NT = NW * 64;
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int TILE = BQ * D * 2;      // bytes of the fp16 Q or dO tile
-  static constexpr int CH = BQ * CPR / NT;     // chunks each thread stages per matrix
-  static constexpr int BUF = 2 * TILE + 2 * BQ * 4;  // one buffer: Q | dO | LSE2 | D
+  static constexpr int LPW = TILE / 1024 / NW; // 1 KiB direct-to-LDS loads per wave per matrix
+  static constexpr int BUF = 2 * TILE + 1024;  // one buffer: Q | dO | statistics
   static constexpr int DS = D / 16, DB = D / 32, QS = BQ / 32, KS = BQ / 16;
-  static_assert(CH >= 1 && BQ * CPR % NT == 0, "tile must split evenly over the threads");
+  static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
+  static_assert(BQ * 8 <= 1024, "one 1 KiB load covers the tile's statistics");
 };
 
 // dK and dV of a block of NW * 32 keys. Per query tile and wave (32 keys):
@@ -84,11 +98,10 @@ struct KvCfg {
 //   P = 2^(c2 S - LSE2), dS = P (dP - D)   (LSE2 = LSE log2 e, +inf for empty rows),
 //   dV^T += dO^T P and dK^T += Q^T dS     (A: transposed LDS reads, B: P / dS
 //                                    packed to fp16 straight from the accumulators).
-// Query tiles are double-buffered: the next tile's global loads are in flight
-// in registers while the current one is computed, then converted to fp16 and
-// written to the other buffer before the one barrier per tile.
+// Query rows at or past N arrive as zeros (Q, dO and both statistics), which
+// makes every term they add zero.
 template <int D>
-__global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF];
 
@@ -102,8 +115,6 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
   const int kl = key_len(p.mask, b, N);
   const int rs = p.H * D;
   const size_t base = ((size_t)b * N * p.H + h) * D;
-  const float* LSE = p.lse + ((size_t)b * p.H + h) * N;
-  const float* DR = p.drow + ((size_t)b * p.H + h) * N;
 
   // This lane's key, and its K and V rows as fp16 B operands:
   // kf[s] = K[key][16 s + 8 hf .. +8). Keys past N are clamped (and masked).
@@ -114,7 +125,7 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
     const size_t off = base + (size_t)min(key, N - 1) * rs + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      kf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.k + off + 16 * s)));
+      kf[s] = ld_global<f16x8_t>((const _Float16*)p.k16 + off + 16 * s);
       vf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + off + 16 * s)));
     }
   }
@@ -138,46 +149,31 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
   const int vqlo = key >= kl ? INT_MAX : (p.mask.wr >= 0 ? key - p.mask.wr : 0);
   const int vqhi = p.mask.wl >= 0 ? key + p.mask.wl : INT_MAX;
 
-  // Staging: chunk u = tid + NT j of a tile is (row u / CPR, chunk u % CPR);
-  // rows at or past N read as zero through the buffer range check.
+  // Direct-to-LDS copies: load j of this wave fills chunks
+  // [(wave * LPW + j) * 64, +64) of a tile, the swizzle applied to the global
+  // chunk each lane fetches; the tile's first row goes in the scalar offset.
+  // Wave 0 also copies the tile's statistics (8 bytes per row).
   const int rs2 = rs * 2;
   const int nbytes = ((N - 1) * rs + D) * 2;
-  const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc((const __bf16*)p.q + base, nbytes);
-  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc((const __bf16*)p.dout + base, nbytes);
-  int gof[C::CH], lof[C::CH];
+  const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc((const _Float16*)p.q16 + base, nbytes);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc((const _Float16*)p.do16 + base, nbytes);
+  const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(p.stats + ((size_t)b * p.H + h) * N * 2, N * 8);
+  int loff[C::LPW];
 #pragma unroll
-  for (int j = 0; j < C::CH; ++j) {
-    const int u = tid + C::NT * j, row = u / C::CPR, c = u % C::CPR;
-    gof[j] = row * rs2 + c * 16;
-    lof[j] = tile_chunk_off<D>(row, c);
+  for (int j = 0; j < C::LPW; ++j) {
+    const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
+    loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
   }
-  u32x4_t qst[C::CH], ost[C::CH];
-  float lst = INFINITY, dst = 0.f;
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    char* sb = smem + buf * C::BUF;
     const int soff = t * C::BQ * rs2;
 #pragma unroll
-    for (int j = 0; j < C::CH; ++j) {
-      qst[j] = buffer_load16(qrsrc, gof[j], soff);
-      ost[j] = buffer_load16(orsrc, gof[j], soff);
+    for (int j = 0; j < C::LPW; ++j) {
+      buffer_load_lds16(qrsrc, sb + (wave * C::LPW + j) * 1024, loff[j], soff);
+      buffer_load_lds16(orsrc, sb + C::TILE + (wave * C::LPW + j) * 1024, loff[j], soff);
     }
-    if (wave == 0) {
-      const int row = t * C::BQ + lane;
-      const float L = LSE[min(row, N - 1)], Dv = DR[min(row, N - 1)];
-      lst = (row >= N || L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;
-      dst = row >= N ? 0.f : Dv;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* sb = smem + buf * C::BUF;
-#pragma unroll
-    for (int j = 0; j < C::CH; ++j) {
-      *(u32x4_t*)(sb + lof[j]) = bf16x8_to_f16x8(qst[j]);
-      *(u32x4_t*)(sb + C::TILE + lof[j]) = bf16x8_to_f16x8(ost[j]);
-    }
-    if (wave == 0) {
-      ((float*)(sb + 2 * C::TILE))[lane] = lst;
-      ((float*)(sb + 2 * C::TILE))[C::BQ + lane] = dst;
-    }
+    if (wave == 0) buffer_load_lds16(srsrc, sb + 2 * C::TILE, lane * 16, t * C::BQ * 8);
   };
 
   // Operand offsets within a tile: row operand of d-step s is row ln, chunk
@@ -192,18 +188,23 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) troff[db][t] = tile_tr_off<D>(lane, db, t);
 
+  // dK^T and dV^T accumulators, kept in AGPRs (see mfma_f16_agpr).
   f32x16_t dk[C::DB], dv[C::DB];
 #pragma unroll
-  for (int d = 0; d < C::DB; ++d) { dk[d] = f32x16_t{}; dv[d] = f32x16_t{}; }
+  for (int d = 0; d < C::DB; ++d) { dk[d] = agpr_zero_acc(); dv[d] = agpr_zero_acc(); }
 
-  auto compute = [&](int t, int buf) {
+  // One query tile. The mask is applied in a branch of its own on tiles that
+  // cross a mask edge; the accumulators never pass through a branch (two
+  // code paths would merge them with AGPR copies the compiler cannot time
+  // against the asm MFMAs).
+  auto compute = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int qb = t * C::BQ;
     if (!(qb < wqhi && qb + C::BQ > wqlo)) return;  // wave-uniform
     const char* sq = smem + buf * C::BUF;
     const char* so = sq + C::TILE;
-    const float* sl = (const float*)(sq + 2 * C::TILE);
-    const float* sd = sl + C::BQ;
-    const bool full = block_all_visible(p.mask, kl, qb, min(qb + C::BQ, N) - 1, wk0, wk1);
+    const float* st = (const float*)(sq + 2 * C::TILE);
+    const bool masked = !block_all_visible(p.mask, kl, qb, min(qb + C::BQ, N) - 1, wk0, wk1);
     u32x4_t pk[C::KS], dsk[C::KS];
 #pragma unroll
     for (int qs = 0; qs < C::QS; ++qs) {
@@ -214,14 +215,15 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
         sa = mfma_f16(*(const f16x8_t*)(sq + off), kf[s], sa);
         pa = mfma_f16(*(const f16x8_t*)(so + off), vf[s], pa);
       }
-      // Element i of a lane is query row 8 (i / 4) + 4 hf + i % 4 of the block.
-      f32x4_t l4[4], d4[4];
+      // Element i of a lane is query row 8 (i / 4) + 4 hf + i % 4 of the
+      // block; st2[2 g + u] holds the statistics of rows 8 g + 4 hf + 2 u, +1.
+      f32x4_t st2[8];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l4[g] = *(const f32x4_t*)(sl + 32 * qs + 8 * g + 4 * hf);
-        d4[g] = *(const f32x4_t*)(sd + 32 * qs + 8 * g + 4 * hf);
-      }
-      if (!full) {
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          st2[2 * g + u] = *(const f32x4_t*)(st + 2 * (32 * qs + 8 * g + 4 * hf + 2 * u));
+      if (masked) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = qb + 32 * qs + 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -230,10 +232,11 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
-        const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -l4[i >> 2][(i & 3) + 1]));
-        const float s0 = p0 * (pa[i] - d4[i >> 2][i & 3]);
-        const float s1 = p1 * (pa[i + 1] - d4[i >> 2][(i & 3) + 1]);
+        const f32x4_t r = st2[i >> 1];  // rows of elements i and i + 1: (L2, D, L2, D)
+        const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -r[0]));
+        const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -r[2]));
+        const float s0 = p0 * (pa[i] - r[1]);
+        const float s1 = p1 * (pa[i + 1] - r[3]);
         pk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
         dsk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(s0, s1);
       }
@@ -245,27 +248,40 @@ __global__ void __launch_bounds__(KvCfg<D>::NT) bwd_dkdv_kernel(BwdParams p) {
         const int ro = ks * 16 * C::CPR * 16;
         const u32x2_t o0 = lds_read_tr16(so + ro + troff[d][0]), o1 = lds_read_tr16(so + ro + troff[d][1]);
         const u32x2_t q0 = lds_read_tr16(sq + ro + troff[d][0]), q1 = lds_read_tr16(sq + ro + troff[d][1]);
-        dv[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{o0[0], o0[1], o1[0], o1[1]}),
-                         __builtin_bit_cast(f16x8_t, pk[ks]), dv[d]);
-        dk[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]}),
-                         __builtin_bit_cast(f16x8_t, dsk[ks]), dk[d]);
+        mfma_f16_agpr(dv[d], __builtin_bit_cast(f16x8_t, u32x4_t{o0[0], o0[1], o1[0], o1[1]}),
+                      __builtin_bit_cast(f16x8_t, pk[ks]));
+        mfma_f16_agpr(dk[d], __builtin_bit_cast(f16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]}),
+                      __builtin_bit_cast(f16x8_t, dsk[ks]));
       }
   };
 
-  if (t0 < t1) {
-    load_tile(t0);
-    store_tile(0);
-    __syncthreads();
-  }
-  for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    if (t + 1 < t1) load_tile(t + 1);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // Query tiles alternate between two LDS buffers (tile t0 + i in buffer i % 2):
+  // each interval issues the copy of the next tile, computes the current one,
+  // then waits for the copy and meets the others at the barrier.
+  auto interval = [&](int t, auto cur, auto nxt) {
+    if (t + 1 < t1) issue_tile(t + 1, nxt);
     compute(t, cur);
-    if (t + 1 < t1) store_tile(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  if (t0 < t1) {
+    issue_tile(t0, B0{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = t0; t < t1; t += 2) {
+      interval(t, B0{}, B1{});
+      if (t + 1 < t1) interval(t + 1, B1{}, B0{});
+    }
   }
 
   // Lane holds dK^T / dV^T rows (d) 32 d + 8 g + 4 hf + (0..3) of its key.
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) {
+    agpr_acc_fence(dk[d]);
+    agpr_acc_fence(dv[d]);
+  }
   if (key < N) {
     __bf16* dkrow = (__bf16*)p.dk + base + (size_t)key * rs;
     __bf16* dvrow = (__bf16*)p.dv + base + (size_t)key * rs;
@@ -290,14 +306,11 @@ struct DqCfg {
   static constexpr int NW = D == 128 ? 8 : 4;  // waves per work-group, 32 queries each
   static constexpr int BM = NW * 32;           // query rows per work-group
   static constexpr int BN = 64;                // keys per tile
-  static constexpr int NT = NW * 64;
   static constexpr int CPR = D / 8;
   static constexpr int TILE = BN * D * 2;      // bytes of one K (fp16) or V (bf16) tile
-  static constexpr int CH = BN * CPR / NT;     // K chunks each thread stages
-  static constexpr int LPW = TILE / 1024 / NW; // V: 1 KiB direct-to-LDS loads per wave
+  static constexpr int LPW = TILE / 1024 / NW; // 1 KiB direct-to-LDS loads per wave per matrix
   static constexpr int DS = D / 16, DB = D / 32, KB = BN / 32, KS = BN / 16;
-  static_assert(CH >= 1 && BN * CPR % NT == 0, "K tile must split evenly over the threads");
-  static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "V tile must split into 1 KiB loads");
+  static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
 };
 
 // dQ of a block of NW * 32 queries, in the forward's orientation: per key
@@ -307,11 +320,9 @@ struct DqCfg {
 //   P = 2^(c2 S - LSE2), dS^T = P (dP^T - D),
 //   dQ^T += K^T dS^T                    (A: transposed K reads; B: dS^T packed
 //                                       to fp16 from the accumulators).
-// K is staged through registers (converted to fp16 for the dS product), V is
-// copied global -> LDS directly (its products stay bf16); both are
-// double-buffered with one barrier per tile.
+// K comes from the fp16 copy (its products meet dS), V stays bf16.
 template <int D>
-__global__ void __launch_bounds__(DqCfg<D>::NT) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];  // [buf][K | V]
 
@@ -342,52 +353,33 @@ __global__ void __launch_bounds__(DqCfg<D>::NT) bwd_dq_kernel(BwdParams p) {
     const size_t off = base + (size_t)qrow * rs + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      qf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.q + off + 16 * s)));
+      qf[s] = ld_global<f16x8_t>((const _Float16*)p.q16 + off + 16 * s);
       of[s] = ld_global<bf16x8_t>((const __bf16*)p.dout + off + 16 * s);
     }
   }
-  float lse2, dr;
-  {
-    const size_t r = ((size_t)b * p.H + h) * N + qrow;
-    const float L = p.lse[r];
-    lse2 = (qi >= N || L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;
-    dr = p.drow[r];
-  }
+  const f32x2_t st = ld_global<f32x2_t>(p.stats + 2 * (((size_t)b * p.H + h) * N + qrow));
+  const float lse2 = qi >= N ? INFINITY : st[0], dr = st[1];
 
   const int rs2 = rs * 2;
   const int nbytes = ((N - 1) * rs + D) * 2;
-  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const __bf16*)p.k + base, nbytes);
+  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const _Float16*)p.k16 + base, nbytes);
   const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc((const __bf16*)p.v + base, nbytes);
-  // K staging (as in the dK/dV kernel) and V direct loads (as in the forward:
-  // load j of this wave fills LDS chunks [(wave * LPW + j) * 64, +64), and the
-  // swizzle is applied to the global chunk each lane fetches).
-  int gof[C::CH], lof[C::CH], loff[C::LPW];
-#pragma unroll
-  for (int j = 0; j < C::CH; ++j) {
-    const int u = tid + C::NT * j, row = u / C::CPR, c = u % C::CPR;
-    gof[j] = row * rs2 + c * 16;
-    lof[j] = tile_chunk_off<D>(row, c);
-  }
+  int loff[C::LPW];
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
     loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
   }
-  u32x4_t kst[C::CH];
-  auto load_tile = [&](int t, auto bufc) {
+  auto issue_tile = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
+    char* kd = smem + (2 * buf) * C::TILE + wave * C::LPW * 1024;
+    char* vd = kd + C::TILE;
     const int soff = t * C::BN * rs2;
 #pragma unroll
-    for (int j = 0; j < C::CH; ++j) kst[j] = buffer_load16(krsrc, gof[j], soff);
-    char* vd = smem + (2 * buf + 1) * C::TILE + wave * C::LPW * 1024;
-#pragma unroll
-    for (int j = 0; j < C::LPW; ++j) buffer_load_lds16(vrsrc, vd + j * 1024, loff[j], soff);
-  };
-  auto store_k = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    char* kd = smem + (2 * buf) * C::TILE;
-#pragma unroll
-    for (int j = 0; j < C::CH; ++j) *(u32x4_t*)(kd + lof[j]) = bf16x8_to_f16x8(kst[j]);
+    for (int j = 0; j < C::LPW; ++j) {
+      buffer_load_lds16(krsrc, kd + j * 1024, loff[j], soff);
+      buffer_load_lds16(vrsrc, vd + j * 1024, loff[j], soff);
+    }
   };
 
   int roff[C::DS];
@@ -409,7 +401,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NT) bwd_dq_kernel(BwdParams p) {
     const char* sv = sk + C::TILE;
     const int kt = t * C::BN;
     if (!(kt < wkhi && kt + C::BN > wklo)) return;  // wave-uniform
-    const bool full = block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1);
+    const bool masked = !block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1);
     u32x4_t dsk[C::KS];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
@@ -420,7 +412,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NT) bwd_dq_kernel(BwdParams p) {
         sa = mfma_f16(*(const f16x8_t*)(sk + off), qf[s], sa);
         pa = mfma_bf16(*(const bf16x8_t*)(sv + off), of[s], pa);
       }
-      if (!full) {
+      if (masked) {
         int lo, hi;
         visible_span(p.mask, kl, qi, lo, hi);
 #pragma unroll
@@ -449,17 +441,14 @@ __global__ void __launch_bounds__(DqCfg<D>::NT) bwd_dq_kernel(BwdParams p) {
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // Key tiles alternate between two LDS buffers (tile t0 + i in buffer i % 2).
   auto interval = [&](int t, auto cur, auto nxt) {
-    if (t + 1 < t1) load_tile(t + 1, nxt);
+    if (t + 1 < t1) issue_tile(t + 1, nxt);
     compute(t, cur);
-    if (t + 1 < t1) store_k(nxt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
   if (t0 < t1) {
-    load_tile(t0, B0{});
-    store_k(B0{});
+    issue_tile(t0, B0{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int t = t0; t < t1; t += 2) {
@@ -488,12 +477,14 @@ template <int D>
 static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.N * p.H;
   const long long rpb = 256 / (D / 8);
-  hipLaunchKernelGGL(bwd_drow_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
                      stream, p);
   p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(KvCfg<D>::NT), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(KvCfg<D>::NW * 64), 0,
+                     stream, p);
   p.nblk = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NT), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -39,7 +39,12 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* drow;           // workspace: D_i = sum_d dO_id O_id, [B][H][N] fp32
+  // Workspace, written by the pre-pass:
+  float* stats;          // per row (LSE log2 e, or +inf for an empty row; D_i =
+                         // sum_d dO_id O_id), [B][H][N][2] fp32
+  void* q16;             // Q, K and dO in fp16, [B][N][H][D] like the inputs
+  void* k16;
+  void* do16;
   MaskParams mask;
   int B, H, N;
   int nblk;              // blocks per (b, h) along the dimension a kernel tiles

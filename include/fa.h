@@ -94,8 +94,10 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v,
 
 /*
  * fa_backward_workspace_size -- bytes of device workspace fa_backward needs
- * for these sizes (the fp32 row statistic D_i = sum_d dO_id O_id, [batch]
- * [heads][seqlen], rounded up to 256 bytes). Returns 0 for invalid sizes.
+ * for these sizes: per row the fp32 pair (LSE log2 e, D_i = sum_d dO_id O_id),
+ * [batch][heads][seqlen][2], then fp16 copies of Q, K and dO (each
+ * batch*seqlen*heads*headdim*2 bytes), every part rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.
  */
 size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
                                   fa_dtype_t dtype);
@@ -117,6 +119,9 @@ size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
  * The mask arguments must match the forward call that produced out and lse.
  * The result is deterministic: dQ is produced by its own pass over the keys
  * (no atomics), dK and dV by a pass over the queries.
+ * Precision: every product with P or dS as an operand takes fp16 operands
+ * (Q, K and dO are converted from bf16, exactly for magnitudes in fp16's
+ * normal range); Q, K and dO must lie below 65504 in magnitude.
  */
 fa_status_t fa_backward(const void* q, const void* k, const void* v,
                         const void* out, const float* lse, const void* dout,
