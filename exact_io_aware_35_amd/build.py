@@ -49,6 +49,17 @@ def _compile(src: str) -> str:
     return obj
 
 
+def device_asm(src: str, out: str) -> str:
+    """Compile one HIP source to gfx950 assembly with the library's flags
+    (used by the tests that inspect the generated code)."""
+    cmd = [HIPCC] + COMMON + DEVICE + EXTRA.get(src, [])
+    cmd += ["--cuda-device-only", "-S", os.path.join(HERE, "csrc", src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile all sources and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
