@@ -5,7 +5,8 @@ A step is one forward call (tiled QK^T, masked online softmax, P V, O and LSE
 epilogue) over the named workload with inputs resident in HBM. The line printed
 on stdout is one JSON object: TFLOP/s with FLOPs = 4 B H N^2 D (halved for a
 causal mask), the roofline of the forward kernel measured with HIP events on
-the stream it runs on, and the fp64 CPU oracle timed on a bounded sample.
+the stream it runs on, the fp64 CPU oracle timed on a bounded sample, and the
+same shape's backward (timed separately, FLOPs counted as 2.5x the forward's).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --extra      # also write fwd/bwd lines for every workload
@@ -253,7 +254,7 @@ def main():
     print(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}",
           file=sys.stderr, flush=True)
 
-    ms, _, (fwd, q) = run_workload(w, args.steps, args.warmup)
+    ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup, backward=True)
     med_ms, mean_ms = per_launch_ms(fwd, min(args.steps, 100))
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -286,6 +287,11 @@ def main():
                      "launch_ms_mean": round(mean_ms, 5), "launch_ms_median": round(med_ms, 5),
                      "algorithmic_bytes": algorithmic_bytes(w)},
         "cpu_baseline": None,
+        # The same shape's backward (prep, dK/dV and dQ kernels), counted as
+        # 2.5x the forward's FLOPs (five N x N x D products against two).
+        "backward": {"ms": round(bwd_ms, 5), "tflops": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 2),
+                     "frac_of_mfma_peak": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),
+                     "flops": 2.5 * flops},
     }
     if args.extra:
         for name, wk in WORKLOADS.items():

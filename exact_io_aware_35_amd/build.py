@@ -27,8 +27,7 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-fno-gpu-rdc", "-munsafe-fp-atomics"]
 # Per-source extras. MFMA results go to arch VGPRs: the kernels read every
 # score accumulator with VALU ops, and the accumulator-register form would add
-# a copy per element. The long-lived dK/dV accumulators of the backward are
-# pinned to AGPRs by hand (fa_common.h, mfma_f16_agpr).
+# a copy per element (the kernels are shaped to fit 256 VGPRs).
 EXTRA = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

@@ -78,6 +78,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV
 
+// One wave per 32 keys; used at headdim 64, where K, V, dK and dV of the
+// wave's keys and the tile's working set fit in 256 VGPRs (two waves per SIMD).
 template <int D>
 struct KvCfg {
   static constexpr int NW = 4;                 // waves per work-group, 32 keys each
@@ -164,7 +166,7 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
     const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
     loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
   }
-  auto issue_tile = [&](int t, auto bufc) {
+  auto issue_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     char* sb = smem + buf * C::BUF;
     const int soff = t * C::BQ * rs2;
@@ -173,7 +175,9 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
       buffer_load_lds16(qrsrc, sb + (wave * C::LPW + j) * 1024, loff[j], soff);
       buffer_load_lds16(orsrc, sb + C::TILE + (wave * C::LPW + j) * 1024, loff[j], soff);
     }
-    if (wave == 0) buffer_load_lds16(srsrc, sb + 2 * C::TILE, lane * 16, t * C::BQ * 8);
+    if (wave == 0)
+      buffer_load_lds16(srsrc, sb + 2 * C::TILE, lane * 16,
+                        __builtin_amdgcn_readfirstlane(t * C::BQ * 8));
   };
 
   // Operand offsets within a tile: row operand of d-step s is row ln, chunk
@@ -188,23 +192,28 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 #pragma unroll
     for (int t = 0; t < 2; ++t) troff[db][t] = tile_tr_off<D>(lane, db, t);
 
-  // dK^T and dV^T accumulators, kept in AGPRs (see mfma_f16_agpr).
-  f32x16_t dk[C::DB], dv[C::DB];
+  f32x16_t dk[C::DB], dv[C::DB];  // dK^T, dV^T (rows d, column = this lane's key)
 #pragma unroll
-  for (int d = 0; d < C::DB; ++d) { dk[d] = agpr_zero_acc(); dv[d] = agpr_zero_acc(); }
+  for (int d = 0; d < C::DB; ++d) { dk[d] = f32x16_t{}; dv[d] = f32x16_t{}; }
 
-  // One query tile. The mask is applied in a branch of its own on tiles that
-  // cross a mask edge; the accumulators never pass through a branch (two
-  // code paths would merge them with AGPR copies the compiler cannot time
-  // against the asm MFMAs).
-  auto compute = [&](int t, auto bufc) {
+  // One query tile. Tiles that every key of the work-group sees in full run
+  // the EDGE = false body: one straight-line block with no branch, which lets
+  // the scheduler overlap one sub-block's exponentials with another's MFMAs.
+  // Other tiles run the EDGE = true body, which skips a wave with nothing to
+  // do and applies the per-element mask in a branch when the wave's keys
+  // need it.
+  auto compute = [&](int t, auto bufc, auto edgec) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    constexpr bool EDGE = decltype(edgec)::value;
     const int qb = t * C::BQ;
-    if (!(qb < wqhi && qb + C::BQ > wqlo)) return;  // wave-uniform
+    bool masked = false;
+    if constexpr (EDGE) {
+      if (!(qb < wqhi && qb + C::BQ > wqlo)) return;  // wave-uniform
+      masked = !block_all_visible(p.mask, kl, qb, min(qb + C::BQ, N) - 1, wk0, wk1);
+    }
     const char* sq = smem + buf * C::BUF;
     const char* so = sq + C::TILE;
     const float* st = (const float*)(sq + 2 * C::TILE);
-    const bool masked = !block_all_visible(p.mask, kl, qb, min(qb + C::BQ, N) - 1, wk0, wk1);
     u32x4_t pk[C::KS], dsk[C::KS];
 #pragma unroll
     for (int qs = 0; qs < C::QS; ++qs) {
@@ -223,7 +232,7 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 #pragma unroll
         for (int u = 0; u < 2; ++u)
           st2[2 * g + u] = *(const f32x4_t*)(st + 2 * (32 * qs + 8 * g + 4 * hf + 2 * u));
-      if (masked) {
+      if (EDGE && masked) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = qb + 32 * qs + 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -248,10 +257,10 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
         const int ro = ks * 16 * C::CPR * 16;
         const u32x2_t o0 = lds_read_tr16(so + ro + troff[d][0]), o1 = lds_read_tr16(so + ro + troff[d][1]);
         const u32x2_t q0 = lds_read_tr16(sq + ro + troff[d][0]), q1 = lds_read_tr16(sq + ro + troff[d][1]);
-        mfma_f16_agpr(dv[d], __builtin_bit_cast(f16x8_t, u32x4_t{o0[0], o0[1], o1[0], o1[1]}),
-                      __builtin_bit_cast(f16x8_t, pk[ks]));
-        mfma_f16_agpr(dk[d], __builtin_bit_cast(f16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]}),
-                      __builtin_bit_cast(f16x8_t, dsk[ks]));
+        dv[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{o0[0], o0[1], o1[0], o1[1]}),
+                      __builtin_bit_cast(f16x8_t, pk[ks]), dv[d]);
+        dk[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]}),
+                      __builtin_bit_cast(f16x8_t, dsk[ks]), dk[d]);
       }
   };
 
@@ -260,27 +269,44 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
   // Query tiles alternate between two LDS buffers (tile t0 + i in buffer i % 2):
   // each interval issues the copy of the next tile, computes the current one,
   // then waits for the copy and meets the others at the barrier.
-  auto interval = [&](int t, auto cur, auto nxt) {
+  auto interval = [&](int t, auto cur, auto nxt, auto edgec) __attribute__((always_inline)) {
     if (t + 1 < t1) issue_tile(t + 1, nxt);
-    compute(t, cur);
+    compute(t, cur, edgec);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
+  auto run = [&](int ta, int tb, auto edgec) __attribute__((always_inline)) {
+    int t = ta;
+    if (t < tb && ((t - t0) & 1)) interval(t++, B1{}, B0{}, edgec);
+    for (; t < tb; t += 2) {
+      interval(t, B0{}, B1{}, edgec);
+      if (t + 1 < tb) interval(t + 1, B1{}, B0{}, edgec);
+    }
+  };
+  // [ta, tb): the tiles every key of the block sees in full (a contiguous
+  // range: a causal or right window bound cuts the front, a left window the
+  // back, key padding inside the block removes it).
+  int ta = t1, tb = t1;
+  if (k0 + C::BK - 1 < kl) {
+    const int kb = k0 + C::BK - 1;
+    ta = p.mask.wr >= 0 ? max(t0, (max(kb - p.mask.wr, 0) + C::BQ - 1) / C::BQ) : t0;
+    tb = (p.mask.wl >= 0 && k0 + p.mask.wl < N - 1) ? (k0 + p.mask.wl + 1) / C::BQ : t1;
+    ta = min(ta, t1);
+    tb = max(min(tb, t1), ta);
+  }
   if (t0 < t1) {
     issue_tile(t0, B0{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int t = t0; t < t1; t += 2) {
-      interval(t, B0{}, B1{});
-      if (t + 1 < t1) interval(t + 1, B1{}, B0{});
-    }
+    run(t0, ta, std::true_type{});
+    run(ta, tb, std::false_type{});
+    run(tb, t1, std::true_type{});
   }
 
   // Lane holds dK^T / dV^T rows (d) 32 d + 8 g + 4 hf + (0..3) of its key.
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) {
-    agpr_acc_fence(dk[d]);
-    agpr_acc_fence(dv[d]);
+
   }
   if (key < N) {
     __bf16* dkrow = (__bf16*)p.dk + base + (size_t)key * rs;
@@ -295,6 +321,289 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
                     pack_bf16x2(dk[d][4 * g + 2] * p.scale, dk[d][4 * g + 3] * p.scale)};
         *(u32x2_t*)(dvrow + col) = u32x2_t{pack_bf16x2(dv[d][4 * g], dv[d][4 * g + 1]),
                                            pack_bf16x2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV (wave pairs)
+
+template <int D>
+struct KvPairCfg {
+  static constexpr int NP = 4;                 // wave pairs per work-group, 32 keys each
+  static constexpr int NW = 2 * NP;            // waves per work-group
+  static constexpr int BK = NP * 32;           // keys per work-group
+  static constexpr int BQ = 64;                // query rows per tile
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BQ * D * 2;      // bytes of the fp16 Q or dO tile
+  static constexpr int LPW = TILE / 1024 / NW; // 1 KiB direct-to-LDS loads per wave per matrix
+  static constexpr int BUF = 2 * TILE + 1024;  // one buffer: Q | dO | statistics
+  static constexpr int XCH = (BQ / 16) * 64 * 16;  // one pair's P: KS 16-byte operands per lane
+  static constexpr int DS = D / 16, DB = D / 32, QS = BQ / 32, KS = BQ / 16;
+  static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
+};
+
+// dK and dV with the work of 32 keys split over a pair of waves, so that
+// each wave needs few enough registers for two waves to share a SIMD (at
+// headdim 128 the one-wave form above holds K, V, dK and dV of its keys in
+// more than the 256 VGPRs a wave can address):
+//   wave 0 of a pair: S = Q K^T, P = 2^(c2 S - LSE2) (masked), P to LDS,
+//                     then dV^T += dO^T P;
+//   wave 1 of a pair: dP = dO V^T, then reads P back and forms
+//                     dS = P (dP - D), then dK^T += Q^T dS.
+// A work-group barrier between the two phases of a tile hands P over; the
+// MFMA work is the same as in the one-wave form. P crosses in fp16, the
+// precision of its own MFMA operand, so dS is formed from the P that dV uses.
+template <int D>
+__global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(BwdParams p) {
+  using C = KvPairCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF + C::NP * C::XCH];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave % C::NP, role = wave / C::NP;
+  const int ln = lane & 31, hf = lane >> 5;
+  int bh, kblk;
+  map_block(p.B * p.H, p.nblk, p.xcd_groups, 0, bh, kblk);
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int N = p.N;
+  const int kl = key_len(p.mask, b, N);
+  const int rs = p.H * D;
+  const size_t base = ((size_t)b * N * p.H + h) * D;
+
+  // This lane's key; the wave's B operand is its K row (role 0) or V row
+  // (role 1) in fp16. Keys past N are clamped (and masked).
+  const int k0 = kblk * C::BK, wk0 = k0 + pair * 32, wk1 = wk0 + 31;
+  const int key = wk0 + ln;
+  f16x8_t kv[C::DS];
+  {
+    const size_t off = base + (size_t)min(key, N - 1) * rs + 8 * hf;
+    if (role == 0) {
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) kv[s] = ld_global<f16x8_t>((const _Float16*)p.k16 + off + 16 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s)
+        kv[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + off + 16 * s)));
+    }
+  }
+
+  // Queries that see a key of the work-group / of this pair: [lo, hi).
+  int qlo = 0, qhi = 0, wqlo = 0, wqhi = 0;
+  {
+    const int klast = min(k0 + C::BK, kl) - 1;
+    if (k0 <= klast) {
+      qlo = p.mask.wr >= 0 ? max(0, k0 - p.mask.wr) : 0;
+      qhi = p.mask.wl >= 0 ? min(N, klast + p.mask.wl + 1) : N;
+    }
+    const int wklast = min(wk1, kl - 1);
+    if (wk0 <= wklast) {
+      wqlo = p.mask.wr >= 0 ? max(0, wk0 - p.mask.wr) : 0;
+      wqhi = p.mask.wl >= 0 ? min(N, wklast + p.mask.wl + 1) : N;
+    }
+  }
+  const int t0 = qlo / C::BQ, t1 = qhi > qlo ? (qhi + C::BQ - 1) / C::BQ : t0;
+  const int vqlo = key >= kl ? INT_MAX : (p.mask.wr >= 0 ? key - p.mask.wr : 0);
+  const int vqhi = p.mask.wl >= 0 ? key + p.mask.wl : INT_MAX;
+
+  const int rs2 = rs * 2;
+  const int nbytes = ((N - 1) * rs + D) * 2;
+  const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc((const _Float16*)p.q16 + base, nbytes);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc((const _Float16*)p.do16 + base, nbytes);
+  const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(p.stats + ((size_t)b * p.H + h) * N * 2, N * 8);
+  int loff[C::LPW];
+#pragma unroll
+  for (int j = 0; j < C::LPW; ++j) {
+    const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
+    loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
+  }
+  auto issue_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    char* sb = smem + buf * C::BUF;
+    const int soff = t * C::BQ * rs2;
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) {
+      buffer_load_lds16(qrsrc, sb + (wave * C::LPW + j) * 1024, loff[j], soff);
+      buffer_load_lds16(orsrc, sb + C::TILE + (wave * C::LPW + j) * 1024, loff[j], soff);
+    }
+    if (wave == 0)
+      buffer_load_lds16(srsrc, sb + 2 * C::TILE, lane * 16,
+                        __builtin_amdgcn_readfirstlane(t * C::BQ * 8));
+  };
+
+  int roff[C::DS];
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s) roff[s] = tile_chunk_off<D>(ln, 2 * s + hf);
+  int troff[C::DB][2];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) troff[db][t] = tile_tr_off<D>(lane, db, t);
+
+  f32x16_t acc[C::DB];  // role 0: dV^T, role 1: dK^T (rows d, column = this lane's key)
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) acc[d] = f32x16_t{};
+  char* xch = smem + 2 * C::BUF + pair * C::XCH;  // this pair's P, [ks][lane] 16 bytes
+
+  // One query tile (EDGE as in the one-wave form). Both waves of every pair
+  // reach the hand-over barrier, active or not.
+  auto compute = [&](int t, auto bufc, auto edgec) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    constexpr bool EDGE = decltype(edgec)::value;
+    const int qb = t * C::BQ;
+    bool active = true, masked = false;
+    if constexpr (EDGE) {
+      active = qb < wqhi && qb + C::BQ > wqlo;  // wave-uniform
+      masked = !block_all_visible(p.mask, kl, qb, min(qb + C::BQ, N) - 1, wk0, wk1);
+    }
+    const char* sq = smem + buf * C::BUF;
+    const char* so = sq + C::TILE;
+    const float* st = (const float*)(sq + 2 * C::TILE);
+    u32x4_t pk[C::KS];    // role 0: P as fp16 B operands
+    f32x16_t pa[C::QS];   // role 1: dP
+    if (active) {
+      if (role == 0) {
+#pragma unroll
+        for (int qs = 0; qs < C::QS; ++qs) {
+          f32x16_t sa = f32x16_t{};
+#pragma unroll
+          for (int s = 0; s < C::DS; ++s)
+            sa = mfma_f16(*(const f16x8_t*)(sq + qs * 32 * C::CPR * 16 + roff[s]), kv[s], sa);
+          f32x4_t st2[8];  // (LSE2, D) of rows 8 g + 4 hf + 2 u, +1 at st2[2 g + u]
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              st2[2 * g + u] = *(const f32x4_t*)(st + 2 * (32 * qs + 8 * g + 4 * hf + 2 * u));
+          if (EDGE && masked) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int row = qb + 32 * qs + 8 * (i >> 2) + 4 * hf + (i & 3);
+              sa[i] = (row >= vqlo) & (row <= vqhi) ? sa[i] : -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const f32x4_t r = st2[i >> 1];
+            const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -r[0]));
+            const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -r[2]));
+            pk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) *(u32x4_t*)(xch + (ks * 64 + lane) * 16) = pk[ks];
+      } else {
+#pragma unroll
+        for (int qs = 0; qs < C::QS; ++qs) {
+          f32x16_t a = f32x16_t{};
+#pragma unroll
+          for (int s = 0; s < C::DS; ++s)
+            a = mfma_f16(*(const f16x8_t*)(so + qs * 32 * C::CPR * 16 + roff[s]), kv[s], a);
+          pa[qs] = a;
+        }
+      }
+    }
+    __syncthreads();  // P of every pair is in LDS
+    if (active) {
+      if (role == 0) {
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const int ro = ks * 16 * C::CPR * 16;
+            const u32x2_t o0 = lds_read_tr16(so + ro + troff[d][0]), o1 = lds_read_tr16(so + ro + troff[d][1]);
+            acc[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{o0[0], o0[1], o1[0], o1[1]}),
+                              __builtin_bit_cast(f16x8_t, pk[ks]), acc[d]);
+          }
+      } else {
+        u32x4_t dsk[C::KS];
+#pragma unroll
+        for (int qs = 0; qs < C::QS; ++qs) {
+          f32x4_t st2[8];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              st2[2 * g + u] = *(const f32x4_t*)(st + 2 * (32 * qs + 8 * g + 4 * hf + 2 * u));
+#pragma unroll
+          for (int hk = 0; hk < 2; ++hk) {
+            const int ks = 2 * qs + hk;
+            const u32x4_t pp = *(const u32x4_t*)(xch + (ks * 64 + lane) * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 8 * hk + 2 * e;  // elements i, i + 1 of this qs
+              const f16x8_t ph = __builtin_bit_cast(f16x8_t, pp);
+              const f32x4_t r = st2[i >> 1];
+              const float s0 = (float)ph[2 * e] * (pa[qs][i] - r[1]);
+              const float s1 = (float)ph[2 * e + 1] * (pa[qs][i + 1] - r[3]);
+              dsk[ks][e] = pack_f16x2(s0, s1);
+            }
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const int ro = ks * 16 * C::CPR * 16;
+            const u32x2_t q0 = lds_read_tr16(sq + ro + troff[d][0]), q1 = lds_read_tr16(sq + ro + troff[d][1]);
+            acc[d] = mfma_f16(__builtin_bit_cast(f16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]}),
+                              __builtin_bit_cast(f16x8_t, dsk[ks]), acc[d]);
+          }
+      }
+    }
+  };
+
+  // Query tiles alternate between two LDS buffers (tile t0 + i in buffer
+  // i % 2): each interval issues the copy of the next tile, computes the
+  // current one, waits for the copy and meets the others at the barrier.
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  auto interval = [&](int t, auto cur, auto nxt, auto edgec) __attribute__((always_inline)) {
+    if (t + 1 < t1) issue_tile(t + 1, nxt);
+    compute(t, cur, edgec);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  auto run = [&](int ta, int tb, auto edgec) __attribute__((always_inline)) {
+    int t = ta;
+    if (t < tb && ((t - t0) & 1)) interval(t++, B1{}, B0{}, edgec);
+    for (; t < tb; t += 2) {
+      interval(t, B0{}, B1{}, edgec);
+      if (t + 1 < tb) interval(t + 1, B1{}, B0{}, edgec);
+    }
+  };
+  // [ta, tb): the tiles every key of the block sees in full (a contiguous
+  // range: a causal or right window bound cuts the front, a left window the
+  // back, key padding inside the block removes it).
+  int ta = t1, tb = t1;
+  if (k0 + C::BK - 1 < kl) {
+    const int kb = k0 + C::BK - 1;
+    ta = p.mask.wr >= 0 ? max(t0, (max(kb - p.mask.wr, 0) + C::BQ - 1) / C::BQ) : t0;
+    tb = (p.mask.wl >= 0 && k0 + p.mask.wl < N - 1) ? (k0 + p.mask.wl + 1) / C::BQ : t1;
+    ta = min(ta, t1);
+    tb = max(min(tb, t1), ta);
+  }
+  if (t0 < t1) {
+    issue_tile(t0, B0{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    run(t0, ta, std::true_type{});
+    run(ta, tb, std::false_type{});
+    run(tb, t1, std::true_type{});
+  }
+
+  // Lane holds dV^T (role 0) or dK^T (role 1) rows 32 d + 8 g + 4 hf + (0..3)
+  // of its key.
+  if (key < N) {
+    const float sc = role == 0 ? 1.f : p.scale;
+    __bf16* row = (__bf16*)(role == 0 ? p.dv : p.dk) + base + (size_t)key * rs;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * d + 8 * g + 4 * hf;
+        *(u32x2_t*)(row + col) =
+            u32x2_t{pack_bf16x2(acc[d][4 * g] * sc, acc[d][4 * g + 1] * sc),
+                    pack_bf16x2(acc[d][4 * g + 2] * sc, acc[d][4 * g + 3] * sc)};
       }
   }
 }
@@ -370,7 +679,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
     const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
     loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
   }
-  auto issue_tile = [&](int t, auto bufc) {
+  auto issue_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     char* kd = smem + (2 * buf) * C::TILE + wave * C::LPW * 1024;
     char* vd = kd + C::TILE;
@@ -395,7 +704,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) dq[d] = f32x16_t{};
 
-  auto compute = [&](int t, auto bufc) {
+  auto compute = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const char* sk = smem + (2 * buf) * C::TILE;
     const char* sv = sk + C::TILE;
@@ -441,7 +750,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  auto interval = [&](int t, auto cur, auto nxt) {
+  auto interval = [&](int t, auto cur, auto nxt) __attribute__((always_inline)) {
     if (t + 1 < t1) issue_tile(t + 1, nxt);
     compute(t, cur);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -479,9 +788,18 @@ static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
   const long long rpb = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
                      stream, p);
-  p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(KvCfg<D>::NW * 64), 0,
-                     stream, p);
+  // Measured on MI355X: the one-wave form is faster at headdim 64 (two
+  // waves per SIMD either way, half the barriers); at headdim 128 only the
+  // pair form keeps its state in VGPRs.
+  if constexpr (D == 128) {
+    p.nblk = (p.N + KvPairCfg<D>::BK - 1) / KvPairCfg<D>::BK;
+    hipLaunchKernelGGL(bwd_dkdv_pair_kernel<D>, dim3(p.B * p.H * p.nblk),
+                       dim3(KvPairCfg<D>::NW * 64), 0, stream, p);
+  } else {
+    p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(KvCfg<D>::NW * 64), 0,
+                       stream, p);
+  }
   p.nblk = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64), 0,
                      stream, p);

@@ -112,33 +112,6 @@ __device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c
 __device__ __forceinline__ f32x16_t mfma_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-// 32x32x16 fp16 MFMA whose accumulator stays in AGPRs (kernels whose live
-// state exceeds the 256 VGPRs keep long-lived accumulators there; the
-// compiler, given the builtin, would copy them to VGPRs and back). The
-// compiler does not see inside the asm, so it carries its own wait states:
-// s_nop 2 covers a VALU write of a, b or acc just before (2 are required);
-// an MFMA reading as C the accumulator the previous one of the same opcode
-// wrote needs none. Reading acc with any other instruction afterwards needs
-// agpr_acc_fence first.
-__device__ __forceinline__ void mfma_f16_agpr(f32x16_t& acc, f16x8_t a, f16x8_t b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// A zero accumulator created in AGPRs (an MFMA with C = 0 and zero inputs),
-// so that every definition of the accumulator is AGPR-constrained and the
-// register allocator keeps it there across loop iterations (volatile: one
-// MFMA per accumulator, never one result copied to several).
-__device__ __forceinline__ f32x16_t agpr_zero_acc() {
-  f32x16_t acc;
-  const f16x8_t z = f16x8_t{};
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
-  return acc;
-}
-// Wait states between the last mfma_f16_agpr writing acc and any other read
-// of it (a 16-pass MFMA result needs 18; 32 are given).
-__device__ __forceinline__ void agpr_acc_fence(f32x16_t& acc) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
-}
-
 __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
