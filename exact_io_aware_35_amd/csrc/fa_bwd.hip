@@ -462,12 +462,17 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
     f32x16_t pa[C::QS];   // role 1: dP
     if (active) {
       if (role == 0) {
+        f32x16_t sall[C::QS];  // the sub-blocks' chains alternate (slack for each operand read)
+#pragma unroll
+        for (int qs = 0; qs < C::QS; ++qs) sall[qs] = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s)
+#pragma unroll
+          for (int qs = 0; qs < C::QS; ++qs)
+            sall[qs] = mfma_f16(*(const f16x8_t*)(sq + qs * 32 * C::CPR * 16 + roff[s]), kv[s], sall[qs]);
 #pragma unroll
         for (int qs = 0; qs < C::QS; ++qs) {
-          f32x16_t sa = f32x16_t{};
-#pragma unroll
-          for (int s = 0; s < C::DS; ++s)
-            sa = mfma_f16(*(const f16x8_t*)(sq + qs * 32 * C::CPR * 16 + roff[s]), kv[s], sa);
+          f32x16_t sa = sall[qs];
           f32x4_t st2[8];  // (LSE2, D) of rows 8 g + 4 hf + 2 u, +1 at st2[2 g + u]
 #pragma unroll
           for (int g = 0; g < 4; ++g)
@@ -493,13 +498,12 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
         for (int ks = 0; ks < C::KS; ++ks) *(u32x4_t*)(xch + (ks * 64 + lane) * 16) = pk[ks];
       } else {
 #pragma unroll
-        for (int qs = 0; qs < C::QS; ++qs) {
-          f32x16_t a = f32x16_t{};
+        for (int qs = 0; qs < C::QS; ++qs) pa[qs] = f32x16_t{};
 #pragma unroll
-          for (int s = 0; s < C::DS; ++s)
-            a = mfma_f16(*(const f16x8_t*)(so + qs * 32 * C::CPR * 16 + roff[s]), kv[s], a);
-          pa[qs] = a;
-        }
+        for (int s = 0; s < C::DS; ++s)
+#pragma unroll
+          for (int qs = 0; qs < C::QS; ++qs)
+            pa[qs] = mfma_f16(*(const f16x8_t*)(so + qs * 32 * C::CPR * 16 + roff[s]), kv[s], pa[qs]);
       }
     }
     __syncthreads();  // P of every pair is in LDS

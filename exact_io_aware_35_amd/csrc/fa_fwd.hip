@@ -165,19 +165,21 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     const int kt = t * C::BN;
     sact = kt < wkhi && kt + C::BN > wklo;
     if (!sact) return;
+    // The 32-key blocks are independent accumulation chains; their MFMAs
+    // alternate so that each chain has a full MFMA of slack for its next
+    // operand read.
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      bf16x8_t kop[C::DS];  // this 32-key block's K operands, read before its MFMAs
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) kop[s] = *(const bf16x8_t*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
+      for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = f32x16_t{};
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
-        f32x16_t acc = f32x16_t{};
+    for (int s = 0; s < C::DS; ++s)
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) acc = mfma_bf16(kop[s], qf[qb][s], acc);
-        sacc[kb][qb] = acc;
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8_t kop = *(const bf16x8_t*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = mfma_bf16(kop, qf[qb][s], sacc[kb][qb]);
       }
-    }
     if (!block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1)) {
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
