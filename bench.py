@@ -29,6 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd/bwd TFLOPS bf16 (B2 H8 N4096 D128) + % of MFMA peak, 1 MI355X"
+METRIC_WORKLOAD_NAME = "fwd_bf16_b2h8n4096d128"
+STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -- python bench.py "
+             "--workload {workload} --steps 200 --warmup 50 --no-cpu-baseline")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
@@ -152,13 +155,36 @@ def summarize(fetch_dir, write_dir, stats_dir, copy_mib, cmds):
            "commands": cmds}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    stats_summary(stats_dir, "fwd_bf16_b2h8n4096d128", cmds["stats"])
+    print(json.dumps(out, indent=1))
+
+
+def stats_summary(stats_dir, workload, cmd):
+    """Copy a rocprofv3 --stats table into profiles/kernel_stats_<workload>.txt."""
+    import glob
     scsv = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     lines = open(scsv).read().strip().splitlines()
-    with open(os.path.join(ROOT, "profiles", "kernel_stats_fwd_bf16_b2h8n4096d128.txt"), "w") as f:
-        f.write("rocprofv3 --kernel-trace --stats summary of the forward on B2 H8 N4096 D128 bf16\n")
-        f.write("command: " + cmds["stats"] + "\n\n")
-        f.write("\n".join(lines) + "\n")
-    print(json.dumps(out, indent=1))
+    # Steady state from the per-dispatch trace: the mean of each kernel's last
+    # 100 launches (the table's averages include the cold warm-up launches).
+    import csv
+    tcsv = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    durs = {}
+    for r in csv.DictReader(open(tcsv)):
+        durs.setdefault(r["Kernel_Name"], []).append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    with open(os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt"), "w") as f:
+        f.write(f"rocprofv3 --kernel-trace --stats summary of bench.py on {workload} "
+                "(forward and backward kernels)\n")
+        f.write("command: " + cmd + "\n\n")
+        f.write("Table from the --stats output (averages over every launch, warm-up included):\n")
+        f.write("\n".join(lines) + "\n\n")
+        f.write("Steady state from the kernel trace (mean / median of the last 100 launches, us):\n")
+        for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            if "fa::" not in name:
+                continue
+            tail = sorted(d[-100:])
+            f.write(f"  {name}: mean {sum(tail) / len(tail) / 1e3:.2f}  "
+                    f"median {tail[len(tail) // 2] / 1e3:.2f}  (launches {len(d)})\n")
 
 
 def cpu_baseline(w, seconds):
@@ -230,13 +256,20 @@ def main():
                     help="after timing, run a plain device copy of this many MiB")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
                     help="write the profiles/ summaries from rocprofv3 output directories")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_DIR", "WORKLOAD"),
+                    help="write profiles/kernel_stats_WORKLOAD.txt from a --stats run of "
+                         "bench.py --workload WORKLOAD")
     args = ap.parse_args()
     if args.summarize:
-        cmd = "rocprofv3 {opts} -- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-mib 256"
+        pmc = "rocprofv3 {opts} -- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-mib 256"
         summarize(*args.summarize, copy_mib=256,
-                  cmds={"fetch": cmd.format(opts="--pmc FETCH_SIZE --output-format csv"),
-                        "write": cmd.format(opts="--pmc WRITE_SIZE --output-format csv"),
-                        "stats": cmd.format(opts="--kernel-trace --stats --output-format csv")})
+                  cmds={"fetch": pmc.format(opts="--pmc FETCH_SIZE --output-format csv"),
+                        "write": pmc.format(opts="--pmc WRITE_SIZE --output-format csv"),
+                        "stats": STATS_CMD.format(workload=METRIC_WORKLOAD_NAME)})
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary[0], args.stats_summary[1],
+                      STATS_CMD.format(workload=args.stats_summary[1]))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -254,7 +287,8 @@ def main():
     print(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}",
           file=sys.stderr, flush=True)
 
-    ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup, backward=True)
+    # The backward is built for bf16 only.
+    ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup, backward=w.dtype == "bf16")
     med_ms, mean_ms = per_launch_ms(fwd, min(args.steps, 100))
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -289,9 +323,10 @@ def main():
         "cpu_baseline": None,
         # The same shape's backward (prep, dK/dV and dQ kernels), counted as
         # 2.5x the forward's FLOPs (five N x N x D products against two).
-        "backward": {"ms": round(bwd_ms, 5), "tflops": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 2),
-                     "frac_of_mfma_peak": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),
-                     "flops": 2.5 * flops},
+        "backward": None if bwd_ms is None else {
+            "ms": round(bwd_ms, 5), "tflops": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 2),
+            "frac_of_mfma_peak": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),
+            "flops": 2.5 * flops},
     }
     if args.extra:
         for name, wk in WORKLOADS.items():
