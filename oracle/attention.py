@@ -26,6 +26,12 @@ Readings where the pages are silent or wrong:
   beside it says a query sees only keys at or before it).
 * Key padding: keys j >= L_b of sequence b are invisible to every query row of
   that sequence; query rows are all still computed.
+* ALiBi ([notes] docstring, ``alibi_slopes``: (nheads,) or (batch, nheads),
+  fp32; a bias -slope * |i - j| is added to the attention score of query i
+  and key j): the bias is added to the scaled score, S = c q.k - slope |i - j|,
+  before masking and softmax. It does not depend on Q or K, so the backward's
+  formulas are unchanged (dS is the gradient of the biased score, and the
+  biased score's derivative in q.k is still c).
 
 Tensors use the (batch, seqlen, nheads, headdim) layout of [notes]. Every
 array argument is converted to float64 first. Parity: pinned by the tests in
@@ -84,36 +90,55 @@ def _softmax_rows(s):
     return p, lse
 
 
-def _scores(qh, kh, scale, vis):
+def _slopes(alibi_slopes, B, H):
+    """ALiBi slopes as a float64 [B, H] array (zeros when there is no bias)."""
+    if alibi_slopes is None:
+        return np.zeros((B, H))
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    if a.shape == (H,):
+        return np.broadcast_to(a, (B, H))
+    if a.shape == (B, H):
+        return a
+    raise ValueError(f"alibi_slopes must have shape ({H},) or ({B}, {H}), got {a.shape}")
+
+
+def _scores(qh, kh, scale, vis, slope=0.0, q_pos=None):
+    """Masked scores c q.k - slope |i - j| of query rows q_pos (default 0..) and keys 0..."""
     s = scale * (qh @ kh.T)
+    if slope != 0.0:
+        i = (np.arange(qh.shape[0]) if q_pos is None else np.asarray(q_pos))[:, None]
+        j = np.arange(kh.shape[0])[None, :]
+        s = s - slope * np.abs(i - j)
     return np.where(vis, s, -np.inf)
 
 
 def attention_forward(q, k, v, softmax_scale=None, causal=False,
-                      window=(-1, -1), seqlens_k=None):
+                      window=(-1, -1), seqlens_k=None, alibi_slopes=None):
     """O [B,N,H,D] and LSE [B,H,N] (natural log) of exact attention.
 
     ``softmax_scale`` defaults to 1/sqrt(headdim) ([notes] docstring).
+    ``alibi_slopes``: None, [H] or [B, H] (see the module notes).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, N, H, D = q.shape
     scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    slopes = _slopes(alibi_slopes, B, H)
     out = np.zeros((B, N, H, D))
     lse = np.zeros((B, H, N))
     for b in range(B):
         vis = visible_mask(N, N, causal, window[0], window[1],
                            _key_len(seqlens_k, b, N))
         for h in range(H):
-            s = _scores(q[b, :, h, :], k[b, :, h, :], scale, vis)
+            s = _scores(q[b, :, h, :], k[b, :, h, :], scale, vis, slopes[b, h])
             p, lse[b, h] = _softmax_rows(s)
             out[b, :, h, :] = p @ v[b, :, h, :]
     return out, lse
 
 
 def attention_forward_rows(q, k, v, rows, softmax_scale=None, causal=False,
-                           window=(-1, -1), seqlens_k=None):
+                           window=(-1, -1), seqlens_k=None, alibi_slopes=None):
     """The same definition evaluated only for query rows ``rows[h]``.
 
     ``rows`` is an int array [H, R] (or [R], shared by all heads) of query
@@ -129,6 +154,7 @@ def attention_forward_rows(q, k, v, rows, softmax_scale=None, causal=False,
         rows = np.broadcast_to(rows, (H, rows.shape[0]))
     R = rows.shape[1]
     scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    slopes = _slopes(alibi_slopes, B, H)
     out = np.zeros((B, H, R, D))
     lse = np.zeros((B, H, R))
     for b in range(B):
@@ -139,14 +165,14 @@ def attention_forward_rows(q, k, v, rows, softmax_scale=None, causal=False,
             qh = np.asarray(q[b, r, h, :], dtype=np.float64)
             kh = np.asarray(k[b, :, h, :], dtype=np.float64)
             vh = np.asarray(v[b, :, h, :], dtype=np.float64)
-            s = _scores(qh, kh, scale, vis)
+            s = _scores(qh, kh, scale, vis, slopes[b, h], q_pos=r)
             p, lse[b, h] = _softmax_rows(s)
             out[b, h] = p @ vh
     return out, lse
 
 
 def attention_backward(q, k, v, dout, softmax_scale=None, causal=False,
-                       window=(-1, -1), seqlens_k=None):
+                       window=(-1, -1), seqlens_k=None, alibi_slopes=None):
     """dQ, dK, dV [B,N,H,D] of exact attention for upstream gradient dO.
 
     P is rebuilt from the definition (the method rebuilds it from the saved
@@ -159,6 +185,7 @@ def attention_backward(q, k, v, dout, softmax_scale=None, causal=False,
     do = np.asarray(dout, dtype=np.float64)
     B, N, H, D = q.shape
     scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    slopes = _slopes(alibi_slopes, B, H)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -167,7 +194,7 @@ def attention_backward(q, k, v, dout, softmax_scale=None, causal=False,
                            _key_len(seqlens_k, b, N))
         for h in range(H):
             qh, kh, vh, doh = q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]
-            p, _ = _softmax_rows(_scores(qh, kh, scale, vis))
+            p, _ = _softmax_rows(_scores(qh, kh, scale, vis, slopes[b, h]))
             dp = doh @ vh.T
             drow = (p * dp).sum(axis=1)
             ds = p * (dp - drow[:, None])

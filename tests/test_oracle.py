@@ -340,3 +340,85 @@ def test_empty_rows_have_zero_gradient():
     dq, dk, dv = attention_backward(q, k, v, do, window=(0, 0), seqlens_k=[5])
     assert (dq[0, 5:] == 0).all() and np.isfinite(dq).all()
     np.testing.assert_allclose(dv[0, :5], do[0, :5], atol=1e-15)
+
+
+# ---------------------------------------------------------------- ALiBi
+
+def _alibi_closed_form(n, slope, causal):
+    """Softmax weights of the scores -slope |i - j| (Q = 0), from geometric
+    sums: Z_i = sum_{d=0}^{i} r^d (+ sum_{d=1}^{n-1-i} r^d without a causal
+    mask), r = e^{-slope}. Returns (W [n, n], ln Z [n])."""
+    r = math.exp(-slope)
+    w = np.zeros((n, n))
+    lnz = np.zeros(n)
+    for i in range(n):
+        z = (1 - r ** (i + 1)) / (1 - r)
+        if not causal:
+            z += r * (1 - r ** (n - 1 - i)) / (1 - r)
+        lnz[i] = math.log(z)
+        for j in range(n):
+            if causal and j > i:
+                continue
+            w[i, j] = r ** abs(i - j) / z
+    return w, lnz
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alibi_zero_query_closed_form(causal):
+    # Q = 0 leaves only the bias: O_i = sum_j w_ij V_j with geometric weights;
+    # a softmax scale other than 1 must not scale the bias.
+    n, d, h = 20, 6, 2
+    slopes = np.array([[0.5, 0.125]])  # [B=1, H=2]
+    v = rnd((1, n, h, d), 90)
+    o, lse = attention_forward(np.zeros((1, n, h, d)), rnd((1, n, h, d), 91), v,
+                               softmax_scale=0.37, causal=causal, alibi_slopes=slopes)
+    for hh in range(h):
+        w, lnz = _alibi_closed_form(n, slopes[0, hh], causal)
+        np.testing.assert_allclose(lse[0, hh], lnz, atol=1e-12)
+        np.testing.assert_allclose(o[0, :, hh], w @ v[0, :, hh], atol=1e-12)
+
+
+def test_alibi_zero_slope_is_plain_attention():
+    shape = (2, 17, 3, 5)
+    q, k, v, do = (rnd(shape, 92 + i) for i in range(4))
+    for kw in [dict(), dict(causal=True, window=(4, 0))]:
+        o0, l0 = attention_forward(q, k, v, **kw)
+        o1, l1 = attention_forward(q, k, v, alibi_slopes=np.zeros(3), **kw)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+        for a, b in zip(attention_backward(q, k, v, do, **kw),
+                        attention_backward(q, k, v, do, alibi_slopes=np.zeros((2, 3)), **kw)):
+            assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alibi_matches_torch_sdpa_float_mask(causal):
+    # torch's fp64 SDPA adds a float attn_mask to the scaled scores.
+    B, N, H, D = 2, 23, 2, 8
+    q, k, v = (rnd((B, N, H, D), 96 + i) for i in range(3))
+    slopes = np.array([[0.25, 0.0625], [1.0, 0.5]])
+    o, _ = attention_forward(q, k, v, causal=causal, alibi_slopes=slopes)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    bias = -slopes[:, :, None, None] * np.abs(i - j)[None, None]
+    if causal:
+        bias = np.where(j <= i, bias, -np.inf)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.tensor(x.transpose(0, 2, 1, 3)) for x in (q, k, v)), attn_mask=torch.tensor(bias))
+    np.testing.assert_allclose(o, ref.numpy().transpose(0, 2, 1, 3), atol=1e-12)
+
+
+def test_alibi_rows_match_full():
+    shape = (1, 40, 2, 4)
+    q, k, v = rnd(shape, 99), rnd(shape, 100), rnd(shape, 101)
+    rows = np.array([[0, 7, 39], [3, 20, 38]])
+    kw = dict(causal=True, window=(9, 0), alibi_slopes=np.array([0.3, 0.05]))
+    o, l = attention_forward(q, k, v, **kw)
+    orow, lrow = attention_forward_rows(q, k, v, rows, **kw)
+    for h in range(2):
+        np.testing.assert_allclose(orow[0, h], o[0, rows[h], h], atol=1e-14)
+        np.testing.assert_allclose(lrow[0, h], l[0, h, rows[h]], atol=1e-14)
+
+
+@pytest.mark.parametrize("kw", [dict(alibi_slopes=[0.4]), dict(causal=True, alibi_slopes=[1.5])])
+def test_alibi_backward_finite_differences(kw):
+    _fd_check((1, 8, 1, 4), kw, 110)

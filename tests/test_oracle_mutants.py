@@ -30,6 +30,9 @@ MUTANTS = {
     "bwd_dk_transposed": ("dk[b, :, h] = scale * (ds.T @ qh)", "dk[b, :, h] = scale * (ds @ qh)"),
     "bwd_dv_untransposed": ("dv[b, :, h] = p.T @ doh", "dv[b, :, h] = p @ doh"),
     "bwd_dp_transposed": ("dp = doh @ vh.T", "dp = (doh @ vh.T).T"),
+    "alibi_sign": ("s = s - slope * np.abs(i - j)", "s = s + slope * np.abs(i - j)"),
+    "alibi_scaled": ("s = s - slope * np.abs(i - j)", "s = s - scale * slope * np.abs(i - j)"),
+    "alibi_no_abs": ("s = s - slope * np.abs(i - j)", "s = s - slope * (i - j)"),
 }
 
 
@@ -64,6 +67,19 @@ def _pins(m):
             ok &= np.allclose(o[0, i, 0], v[0, vis, 0].mean(axis=0), atol=1e-12)
             ok &= abs(lse[0, 0, i] - math.log(len(vis))) < 1e-12
         yield "zero_q", ok
+    # ALiBi with Q = 0: weights r^|i-j| / Z_i, r = e^-slope (geometric sums).
+    for causal, slope in [(True, 0.5), (False, 0.25)]:
+        o, lse = m.attention_forward(np.zeros((1, n, 1, d)), k, v, softmax_scale=0.6,
+                                     causal=causal, alibi_slopes=[slope])
+        r = math.exp(-slope)
+        ok = True
+        for i in range(n):
+            js = range(i + 1) if causal else range(n)
+            wts = np.array([r ** abs(i - j) for j in js])
+            ok &= abs(lse[0, 0, i] - math.log(wts.sum())) < 1e-12
+            ok &= np.allclose(o[0, i, 0], (wts[:, None] * v[0, list(js), 0]).sum(0) / wts.sum(),
+                              atol=1e-12)
+        yield "alibi_zero_q", ok
     # Causal first row: LSE_0 = c q0.k0.
     q = rnd((1, n, 1, d), 3)
     o, lse = m.attention_forward(q, k, v, softmax_scale=0.7, causal=True)
