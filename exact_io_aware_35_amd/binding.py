@@ -34,6 +34,10 @@ SIGNATURES = [
     ("fa_backward_workspace_size", _SZ, [_I, _I, _I, _I, _I]),
     ("fa_backward", _I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I,
                          _I, _P, _SZ, _P]),
+    ("fa_forward_ex", _I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
+                           _P]),
+    ("fa_backward_ex", _I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                            _F, _I, _I, _I, _I, _P, _SZ, _P]),
     ("fa_status_string", ctypes.c_char_p, [_I]),
     ("fa_last_error_message", ctypes.c_char_p, []),
 ]
@@ -96,30 +100,65 @@ def _dev_ptr(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _alibi(alibi_slopes, batch, heads):
+    """(pointer, batch stride) of optional ALiBi slopes: fp32 device [H] or [B, H]."""
+    import torch
+    if alibi_slopes is None:
+        return None, 0
+    if alibi_slopes.dtype != torch.float32:
+        raise FaError(FA_ERR_INVALID_ARG, "alibi_slopes must be float32")
+    if tuple(alibi_slopes.shape) == (heads,):
+        stride = 0
+    elif tuple(alibi_slopes.shape) == (batch, heads):
+        stride = heads
+    else:
+        raise FaError(FA_ERR_INVALID_ARG,
+                      f"alibi_slopes must have shape ({heads},) or ({batch}, {heads})")
+    return _dev_ptr(alibi_slopes, "alibi_slopes"), stride
+
+
+def _forward(q, k, v, packed, shape, causal, window, softmax_scale, seqlens_k, alibi_slopes,
+             out, lse, stream):
+    import torch
+    lib = load_library()
+    B, N, H, D = shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty(shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    slopes, bstride = _alibi(alibi_slopes, B, H)
+    st = lib.fa_forward_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), int(packed),
+                           _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                           _dev_ptr(seqlens_k, "seqlens_k"), slopes, bstride, B, H, N, D, scale,
+                           int(bool(causal)), int(window[0]), int(window[1]), _dtype_code(q),
+                           _stream_handle(stream, q.device))
+    _check(lib, st)
+    return out, lse
+
+
 def forward(q, k, v, causal=False, window=(-1, -1), softmax_scale=None, seqlens_k=None,
-            out=None, lse=None, stream=None):
+            alibi_slopes=None, out=None, lse=None, stream=None):
     """O, LSE = exact attention of q, k, v ([batch, seqlen, heads, headdim]).
 
     softmax_scale defaults to 1/sqrt(headdim). seqlens_k: int32 [batch] key
-    lengths on the device, or None. Returns (out, lse) with lse [B, H, N] fp32.
+    lengths on the device, or None. alibi_slopes: fp32 [heads] or [batch,
+    heads] on the device, or None. Returns (out, lse) with lse [B, H, N] fp32.
     """
-    import torch
-    lib = load_library()
-    B, N, H, D = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise FaError(FA_ERR_INVALID_ARG, "q, k, v must have the same shape")
-    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    st = lib.fa_forward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                        _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
-                        _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale, int(bool(causal)),
-                        int(window[0]), int(window[1]), _dtype_code(q),
-                        _stream_handle(stream, q.device))
-    _check(lib, st)
-    return out, lse
+    return _forward(q, k, v, False, tuple(q.shape), causal, window, softmax_scale, seqlens_k,
+                    alibi_slopes, out, lse, stream)
+
+
+def forward_qkvpacked(qkv, causal=False, window=(-1, -1), softmax_scale=None, seqlens_k=None,
+                      alibi_slopes=None, out=None, lse=None, stream=None):
+    """forward() of one packed qkv tensor [batch, seqlen, 3, heads, headdim]."""
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise FaError(FA_ERR_INVALID_ARG, "qkv must have shape (batch, seqlen, 3, heads, headdim)")
+    B, N, _, H, D = qkv.shape
+    return _forward(qkv, None, None, True, (B, N, H, D), causal, window, softmax_scale,
+                    seqlens_k, alibi_slopes, out, lse, stream)
 
 
 class PreparedCall:
@@ -160,26 +199,46 @@ def workspace_size(batch, heads, seqlen, headdim, dtype_code=FA_DTYPE_BF16):
     return int(load_library().fa_backward_workspace_size(batch, heads, seqlen, headdim, dtype_code))
 
 
-def backward(q, k, v, out, lse, dout, causal=False, window=(-1, -1), softmax_scale=None,
-             seqlens_k=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV of exact attention, recomputing P from the forward's LSE."""
+def _backward(q, k, v, packed, shape, out, lse, dout, causal, window, softmax_scale, seqlens_k,
+              alibi_slopes, grads, workspace, stream):
     import torch
     lib = load_library()
-    B, N, H, D = q.shape
+    B, N, H, D = shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
     code = _dtype_code(q)
     need = int(lib.fa_backward_workspace_size(B, H, N, D, code))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = lib.fa_backward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                         _dev_ptr(out, "out"), _dev_ptr(lse, "lse"), _dev_ptr(dout, "dout"),
-                         _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
-                         _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale,
-                         int(bool(causal)), int(window[0]), int(window[1]), code,
-                         _dev_ptr(workspace, "workspace"), workspace.numel(),
-                         _stream_handle(stream, q.device))
+    slopes, bstride = _alibi(alibi_slopes, B, H)
+    st = lib.fa_backward_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), int(packed),
+                            _dev_ptr(out, "out"), _dev_ptr(lse, "lse"), _dev_ptr(dout, "dout"),
+                            _dev_ptr(grads[0], "dq"), _dev_ptr(grads[1], "dk"),
+                            _dev_ptr(grads[2], "dv"), _dev_ptr(seqlens_k, "seqlens_k"), slopes,
+                            bstride, B, H, N, D, scale, int(bool(causal)), int(window[0]),
+                            int(window[1]), code, _dev_ptr(workspace, "workspace"),
+                            workspace.numel(), _stream_handle(stream, q.device))
     _check(lib, st)
+
+
+def backward(q, k, v, out, lse, dout, causal=False, window=(-1, -1), softmax_scale=None,
+             seqlens_k=None, alibi_slopes=None, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """dQ, dK, dV of exact attention, recomputing P from the forward's LSE."""
+    import torch
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _backward(q, k, v, False, tuple(q.shape), out, lse, dout, causal, window, softmax_scale,
+              seqlens_k, alibi_slopes, (dq, dk, dv), workspace, stream)
     return dq, dk, dv
+
+
+def backward_qkvpacked(qkv, out, lse, dout, causal=False, window=(-1, -1), softmax_scale=None,
+                       seqlens_k=None, alibi_slopes=None, dqkv=None, workspace=None, stream=None):
+    """dqkv [batch, seqlen, 3, heads, headdim] for a packed qkv input."""
+    import torch
+    B, N, _, H, D = qkv.shape
+    dqkv = torch.empty_like(qkv) if dqkv is None else dqkv
+    _backward(qkv, None, None, True, (B, N, H, D), out, lse, dout, causal, window,
+              softmax_scale, seqlens_k, alibi_slopes, (dqkv, None, None), workspace, stream)
+    return dqkv

@@ -28,7 +28,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shared size/mask/scale checks. On success fills the folded window bounds.
 fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float scale,
                          int causal, int wl, int wr, fa_dtype_t dtype, int* wl_eff,
-                         int* wr_eff) {
+                         int* wr_eff, int row_mult = 1) {
   if (batch < 1 || heads < 1 || seqlen < 1)
     return fail(FA_ERR_INVALID_ARG, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)",
                 batch, heads, seqlen);
@@ -42,10 +42,11 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
     return fail(FA_ERR_UNSUPPORTED, "headdim %d is not supported (64 or 128)", headdim);
   // Kernels address one (batch, head) slice with 32-bit byte offsets (buffer
   // loads take a 32-bit offset); one key tile of slack covers the prefetch.
+  // row_mult is 3 for a packed (batch, seqlen, 3, heads, headdim) input.
   const long long esize = dtype == FA_DTYPE_F32 ? 4 : 2;
-  if (((long long)seqlen + 128) * heads * headdim * esize >= (1LL << 31))
-    return fail(FA_ERR_UNSUPPORTED, "a (batch, head) slice of seqlen*heads*headdim elements "
-                "must span less than 2^31 bytes");
+  if (((long long)seqlen + 128) * row_mult * heads * headdim * esize >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "a (batch, head) slice of seqlen rows of the input must "
+                "span less than 2^31 bytes");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (wl < -1 || wr < -1)
@@ -62,6 +63,49 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
 fa_status_t check_ptr(const void* p, const char* name) {
   if (p == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is null", name);
   if (!aligned16(p)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+// Three per-(q, k, v) pointers of a call and their row stride in elements:
+// three tensors, or one packed (batch, seqlen, 3, heads, headdim) tensor in
+// the first pointer ([notes] docstring, qkv argument) with the other two
+// null. names = {packed name, first, second, third}.
+fa_status_t resolve_qkv(const void* a, const void* b, const void* c, int packed, int heads,
+                        int headdim, fa_dtype_t dtype, const char* const names[4],
+                        void* out[3], int* rs) {
+  fa_status_t s;
+  if (packed) {
+    if ((s = check_ptr(a, names[0])) != FA_OK) return s;
+    if (b != nullptr || c != nullptr)
+      return fail(FA_ERR_INVALID_ARG, "%s and %s must be null when qkv_packed is set", names[2],
+                  names[3]);
+    const size_t step = (size_t)heads * headdim * (dtype == FA_DTYPE_F32 ? 4 : 2);
+    char* base = static_cast<char*>(const_cast<void*>(a));
+    out[0] = base;
+    out[1] = base + step;
+    out[2] = base + 2 * step;
+    *rs = 3 * heads * headdim;
+    return FA_OK;
+  }
+  const void* ptrs[] = {a, b, c};
+  for (int i = 0; i < 3; ++i) {
+    if ((s = check_ptr(ptrs[i], names[i + 1])) != FA_OK) return s;
+    out[i] = const_cast<void*>(ptrs[i]);
+  }
+  *rs = heads * headdim;
+  return FA_OK;
+}
+
+const char* const kQkvNames[4] = {"qkv", "q", "k", "v"};
+const char* const kGradNames[4] = {"dqkv", "dq", "dk", "dv"};
+
+// ALiBi slopes: null, or 4-byte aligned with a batch stride of 0 or heads.
+fa_status_t check_alibi(const float* slopes, int bstride, int heads) {
+  if (slopes == nullptr) return FA_OK;
+  if (reinterpret_cast<uintptr_t>(slopes) & 3u)
+    return fail(FA_ERR_INVALID_ARG, "alibi_slopes is not 4-byte aligned");
+  if (bstride != 0 && bstride != heads)
+    return fail(FA_ERR_INVALID_ARG, "alibi_batch_stride must be 0 or heads (got %d)", bstride);
   return FA_OK;
 }
 
@@ -101,29 +145,39 @@ const char* fa_status_string(fa_status_t s) {
 
 const char* fa_last_error_message(void) { return g_msg; }
 
-fa_status_t fa_forward(const void* q, const void* k, const void* v, void* out, float* lse,
-                       const int32_t* seqlens_k, int batch, int heads, int seqlen, int headdim,
-                       float softmax_scale, int causal, int window_left, int window_right,
-                       fa_dtype_t dtype, hipStream_t stream) {
+fa_status_t fa_forward_ex(const void* q, const void* k, const void* v, int qkv_packed,
+                          void* out, float* lse, const int32_t* seqlens_k,
+                          const float* alibi_slopes, int alibi_batch_stride, int batch, int heads,
+                          int seqlen, int headdim, float softmax_scale, int causal,
+                          int window_left, int window_right, fa_dtype_t dtype,
+                          hipStream_t stream) {
   g_msg[0] = '\0';
   int wl, wr;
   fa_status_t s = check_common(batch, heads, seqlen, headdim, softmax_scale, causal,
-                               window_left, window_right, dtype, &wl, &wr);
+                               window_left, window_right, dtype, &wl, &wr, qkv_packed ? 3 : 1);
   if (s != FA_OK) return s;
-  const void* ptrs[] = {q, k, v, out, lse};
-  const char* names[] = {"q", "k", "v", "out", "lse"};
-  for (int i = 0; i < 5; ++i)
-    if ((s = check_ptr(ptrs[i], names[i])) != FA_OK) return s;
+  void* qkv[3];
+  int rs_q;
+  if ((s = resolve_qkv(q, k, v, qkv_packed, heads, headdim, dtype, kQkvNames, qkv, &rs_q)) !=
+      FA_OK)
+    return s;
+  if ((s = check_ptr(out, "out")) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse")) != FA_OK) return s;
   if (seqlens_k != nullptr && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+  if ((s = check_alibi(alibi_slopes, alibi_batch_stride, heads)) != FA_OK) return s;
 
   const int f32 = dtype == FA_DTYPE_F32;
   fa::FwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+  p.q = qkv[0]; p.k = qkv[1]; p.v = qkv[2]; p.o = out; p.lse = lse;
   p.mask.seqlens_k = seqlens_k;
   p.mask.wl = wl;
   p.mask.wr = wr;
+  p.alibi.slopes = alibi_slopes;
+  p.alibi.bstride = alibi_batch_stride;
   p.B = batch; p.H = heads; p.N = seqlen;
+  p.rs_q = rs_q;
+  p.rs_o = heads * headdim;
   const int bm = fa::fwd_block_rows(f32, headdim);
   p.nqb = (seqlen + bm - 1) / bm;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -134,6 +188,14 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* out, f
   hipError_t e = fa::launch_forward(p, headdim, f32, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+fa_status_t fa_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                       const int32_t* seqlens_k, int batch, int heads, int seqlen, int headdim,
+                       float softmax_scale, int causal, int window_left, int window_right,
+                       fa_dtype_t dtype, hipStream_t stream) {
+  return fa_forward_ex(q, k, v, 0, out, lse, seqlens_k, nullptr, 0, batch, heads, seqlen,
+                       headdim, softmax_scale, causal, window_left, window_right, dtype, stream);
 }
 
 size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
@@ -147,25 +209,38 @@ size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
   return bwd_workspace(batch, heads, seqlen, headdim).total;
 }
 
-fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* out,
-                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                        const int32_t* seqlens_k, int batch, int heads, int seqlen, int headdim,
-                        float softmax_scale, int causal, int window_left, int window_right,
-                        fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_packed,
+                           const void* out, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, const int32_t* seqlens_k,
+                           const float* alibi_slopes, int alibi_batch_stride, int batch,
+                           int heads, int seqlen, int headdim, float softmax_scale, int causal,
+                           int window_left, int window_right, fa_dtype_t dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   g_msg[0] = '\0';
   int wl, wr;
   fa_status_t s = check_common(batch, heads, seqlen, headdim, softmax_scale, causal,
-                               window_left, window_right, dtype, &wl, &wr);
+                               window_left, window_right, dtype, &wl, &wr, qkv_packed ? 3 : 1);
   if (s != FA_OK) return s;
   if (dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
-  const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
-  const char* names[] = {"q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"};
-  for (int i = 0; i < 9; ++i)
+  void* qkv[3];
+  int rs_q;
+  if ((s = resolve_qkv(q, k, v, qkv_packed, heads, headdim, dtype, kQkvNames, qkv, &rs_q)) !=
+      FA_OK)
+    return s;
+  // The gradients take the layout of the inputs: dq holds the packed dqkv.
+  void* grads[3];
+  int rs_g;
+  if ((s = resolve_qkv(dq, dk, dv, qkv_packed, heads, headdim, dtype, kGradNames, grads,
+                       &rs_g)) != FA_OK)
+    return s;
+  const void* ptrs[] = {out, lse, dout};
+  const char* names[] = {"out", "lse", "dout"};
+  for (int i = 0; i < 3; ++i)
     if ((s = check_ptr(ptrs[i], names[i])) != FA_OK) return s;
   if (seqlens_k != nullptr && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+  if ((s = check_alibi(alibi_slopes, alibi_batch_stride, heads)) != FA_OK) return s;
   const BwdWorkspace ws = bwd_workspace(batch, heads, seqlen, headdim);
   const size_t need = ws.total;
   if (workspace == nullptr || workspace_bytes < need)
@@ -174,8 +249,10 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
   if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
 
   fa::BwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = out; p.dout = dout; p.lse = lse;
-  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.q = qkv[0]; p.k = qkv[1]; p.v = qkv[2]; p.o = out; p.dout = dout; p.lse = lse;
+  p.dq = grads[0];
+  p.dk = grads[1];
+  p.dv = grads[2];
   char* wsb = static_cast<char*>(workspace);
   p.stats = reinterpret_cast<float*>(wsb + ws.stats);
   p.q16 = wsb + ws.q16;
@@ -184,13 +261,29 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v, const void*
   p.mask.seqlens_k = seqlens_k;
   p.mask.wl = wl;
   p.mask.wr = wr;
+  p.alibi.slopes = alibi_slopes;
+  p.alibi.bstride = alibi_batch_stride;
   p.B = batch; p.H = heads; p.N = seqlen;
+  p.rs_q = rs_q;
+  p.rs_o = heads * headdim;
+  p.rs_g = rs_g;
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.xcd_groups = (batch * heads) % 8 == 0 ? 1 : 0;
   hipError_t e = fa::launch_backward(p, headdim, dtype == FA_DTYPE_F32, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+fa_status_t fa_backward(const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        const int32_t* seqlens_k, int batch, int heads, int seqlen, int headdim,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return fa_backward_ex(q, k, v, 0, out, lse, dout, dq, dk, dv, seqlens_k, nullptr, 0, batch,
+                        heads, seqlen, headdim, softmax_scale, causal, window_left, window_right,
+                        dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -52,11 +52,14 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   const long long R = (long long)p.B * p.N * p.H;
   float acc = 0.f;
   if (r < R) {
-    const size_t e = (size_t)r * D + 8 * c;
-    const u32x4_t o = ld_global<u32x4_t>((const __bf16*)p.o + e);
-    const u32x4_t g = ld_global<u32x4_t>((const __bf16*)p.dout + e);
-    const u32x4_t q = ld_global<u32x4_t>((const __bf16*)p.q + e);
-    const u32x4_t k = ld_global<u32x4_t>((const __bf16*)p.k + e);
+    const long long bi = r / p.H;                 // b * N + i
+    const size_t hd = (size_t)(r - bi * p.H) * D + 8 * c;
+    const size_t e = (size_t)r * D + 8 * c;       // the fp16 copies are [B][N][H][D]
+    const size_t eq = (size_t)bi * p.rs_q + hd, eo = (size_t)bi * p.rs_o + hd;
+    const u32x4_t o = ld_global<u32x4_t>((const __bf16*)p.o + eo);
+    const u32x4_t g = ld_global<u32x4_t>((const __bf16*)p.dout + eo);
+    const u32x4_t q = ld_global<u32x4_t>((const __bf16*)p.q + eq);
+    const u32x4_t k = ld_global<u32x4_t>((const __bf16*)p.k + eq);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc += bf16_lo(o[j]) * bf16_lo(g[j]) + bf16_hi(o[j]) * bf16_hi(g[j]);
@@ -102,7 +105,7 @@ struct KvCfg {
 //                                    packed to fp16 straight from the accumulators).
 // Query rows at or past N arrive as zeros (Q, dO and both statistics), which
 // makes every term they add zero.
-template <int D>
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF];
@@ -115,8 +118,12 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
-  const int rs = p.H * D;
+  const int rs = p.H * D;                               // the fp16 copies
   const size_t base = ((size_t)b * N * p.H + h) * D;
+  const size_t vbase = (size_t)b * N * p.rs_q + (size_t)h * D;
+  const size_t gbase = (size_t)b * N * p.rs_g + (size_t)h * D;
+  float slope2 = 0.f;  // ALiBi slope in the log2 domain of the exponent
+  if constexpr (ALIBI) slope2 = alibi_raw_slope(p.alibi, b, h, p.scale_log2) * p.scale_log2;
 
   // This lane's key, and its K and V rows as fp16 B operands:
   // kf[s] = K[key][16 s + 8 hf .. +8). Keys past N are clamped (and masked).
@@ -124,11 +131,13 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
   const int key = wk0 + ln;
   f16x8_t kf[C::DS], vf[C::DS];
   {
-    const size_t off = base + (size_t)min(key, N - 1) * rs + 8 * hf;
+    const int kr = min(key, N - 1);
+    const size_t off = base + (size_t)kr * rs + 8 * hf;
+    const size_t voff = vbase + (size_t)kr * p.rs_q + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       kf[s] = ld_global<f16x8_t>((const _Float16*)p.k16 + off + 16 * s);
-      vf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + off + 16 * s)));
+      vf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + voff + 16 * s)));
     }
   }
 
@@ -239,11 +248,19 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
           sa[i] = (row >= vqlo) & (row <= vqhi) ? sa[i] : -INFINITY;
         }
       }
+      // ALiBi: the exponent takes -slope log2(e) |i - j| (row i, key j).
+      const float di = (float)(qb + 32 * qs + 4 * hf - key);
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const f32x4_t r = st2[i >> 1];  // rows of elements i and i + 1: (L2, D, L2, D)
-        const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -r[0]));
-        const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -r[2]));
+        float x0 = fmaf(sa[i], p.scale_log2, -r[0]);
+        float x1 = fmaf(sa[i + 1], p.scale_log2, -r[2]);
+        if constexpr (ALIBI) {
+          x0 = fmaf(fabsf(di + (float)(8 * (i >> 2) + (i & 3))), -slope2, x0);
+          x1 = fmaf(fabsf(di + (float)(8 * (i >> 2) + (i & 3) + 1)), -slope2, x1);
+        }
+        const float p0 = exp2_fast(x0);
+        const float p1 = exp2_fast(x1);
         const float s0 = p0 * (pa[i] - r[1]);
         const float s1 = p1 * (pa[i + 1] - r[3]);
         pk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
@@ -309,8 +326,8 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 
   }
   if (key < N) {
-    __bf16* dkrow = (__bf16*)p.dk + base + (size_t)key * rs;
-    __bf16* dvrow = (__bf16*)p.dv + base + (size_t)key * rs;
+    __bf16* dkrow = (__bf16*)p.dk + gbase + (size_t)key * p.rs_g;
+    __bf16* dvrow = (__bf16*)p.dv + gbase + (size_t)key * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
@@ -353,7 +370,7 @@ struct KvPairCfg {
 // A work-group barrier between the two phases of a tile hands P over; the
 // MFMA work is the same as in the one-wave form. P crosses in fp16, the
 // precision of its own MFMA operand, so dS is formed from the P that dV uses.
-template <int D>
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(BwdParams p) {
   using C = KvPairCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF + C::NP * C::XCH];
@@ -367,8 +384,12 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
-  const int rs = p.H * D;
+  const int rs = p.H * D;                               // the fp16 copies
   const size_t base = ((size_t)b * N * p.H + h) * D;
+  const size_t vbase = (size_t)b * N * p.rs_q + (size_t)h * D;
+  const size_t gbase = (size_t)b * N * p.rs_g + (size_t)h * D;
+  float slope_raw = 0.f;
+  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
 
   // This lane's key; the wave's B operand is its K row (role 0) or V row
   // (role 1) in fp16. Keys past N are clamped (and masked).
@@ -376,11 +397,13 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
   const int key = wk0 + ln;
   f16x8_t kv[C::DS];
   {
-    const size_t off = base + (size_t)min(key, N - 1) * rs + 8 * hf;
+    const int kr = min(key, N - 1);
     if (role == 0) {
+      const size_t off = base + (size_t)kr * rs + 8 * hf;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) kv[s] = ld_global<f16x8_t>((const _Float16*)p.k16 + off + 16 * s);
     } else {
+      const size_t off = vbase + (size_t)kr * p.rs_q + 8 * hf;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s)
         kv[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + off + 16 * s)));
@@ -473,6 +496,12 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
 #pragma unroll
         for (int qs = 0; qs < C::QS; ++qs) {
           f32x16_t sa = sall[qs];
+          if constexpr (ALIBI) {  // row i, key j: q.k - (slope / c) |i - j|
+            const float di = (float)(qb + 32 * qs + 4 * hf - key);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              sa[i] = fmaf(fabsf(di + (float)(8 * (i >> 2) + (i & 3))), -slope_raw, sa[i]);
+          }
           f32x4_t st2[8];  // (LSE2, D) of rows 8 g + 4 hf + 2 u, +1 at st2[2 g + u]
 #pragma unroll
           for (int g = 0; g < 4; ++g)
@@ -599,7 +628,7 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
   // of its key.
   if (key < N) {
     const float sc = role == 0 ? 1.f : p.scale;
-    __bf16* row = (__bf16*)(role == 0 ? p.dv : p.dk) + base + (size_t)key * rs;
+    __bf16* row = (__bf16*)(role == 0 ? p.dv : p.dk) + gbase + (size_t)key * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
@@ -634,7 +663,7 @@ struct DqCfg {
 //   dQ^T += K^T dS^T                    (A: transposed K reads; B: dS^T packed
 //                                       to fp16 from the accumulators).
 // K comes from the fp16 copy (its products meet dS), V stays bf16.
-template <int D>
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];  // [buf][K | V]
@@ -647,8 +676,13 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
-  const int rs = p.H * D;
+  const int rs = p.H * D;                               // the fp16 copies
   const size_t base = ((size_t)b * N * p.H + h) * D;
+  const size_t obase = (size_t)b * N * p.rs_o + (size_t)h * D;
+  const size_t vbase = (size_t)b * N * p.rs_q + (size_t)h * D;
+  const size_t gbase = (size_t)b * N * p.rs_g + (size_t)h * D;
+  float slope_raw = 0.f;
+  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
 
   const int q0 = qblk * C::BM, wq0 = q0 + wave * 32;
   int klo, khi;
@@ -664,34 +698,37 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   bf16x8_t of[C::DS];
   {
     const size_t off = base + (size_t)qrow * rs + 8 * hf;
+    const size_t ooff = obase + (size_t)qrow * p.rs_o + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       qf[s] = ld_global<f16x8_t>((const _Float16*)p.q16 + off + 16 * s);
-      of[s] = ld_global<bf16x8_t>((const __bf16*)p.dout + off + 16 * s);
+      of[s] = ld_global<bf16x8_t>((const __bf16*)p.dout + ooff + 16 * s);
     }
   }
   const f32x2_t st = ld_global<f32x2_t>(p.stats + 2 * (((size_t)b * p.H + h) * N + qrow));
   const float lse2 = qi >= N ? INFINITY : st[0], dr = st[1];
 
-  const int rs2 = rs * 2;
-  const int nbytes = ((N - 1) * rs + D) * 2;
-  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc((const _Float16*)p.k16 + base, nbytes);
-  const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc((const __bf16*)p.v + base, nbytes);
-  int loff[C::LPW];
+  // K (fp16 copy) and V (input) rows sit rs and rs_q elements apart.
+  const int krs2 = rs * 2, vrs2 = p.rs_q * 2;
+  const __amdgpu_buffer_rsrc_t krsrc =
+      make_rsrc((const _Float16*)p.k16 + base, ((N - 1) * rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      make_rsrc((const __bf16*)p.v + vbase, ((N - 1) * p.rs_q + D) * 2);
+  int kloff[C::LPW], vloff[C::LPW];
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
-    loff[j] = row * rs2 + (pos ^ lds_swz<D>(row)) * 16;
+    kloff[j] = row * krs2 + (pos ^ lds_swz<D>(row)) * 16;
+    vloff[j] = row * vrs2 + (pos ^ lds_swz<D>(row)) * 16;
   }
   auto issue_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     char* kd = smem + (2 * buf) * C::TILE + wave * C::LPW * 1024;
     char* vd = kd + C::TILE;
-    const int soff = t * C::BN * rs2;
 #pragma unroll
     for (int j = 0; j < C::LPW; ++j) {
-      buffer_load_lds16(krsrc, kd + j * 1024, loff[j], soff);
-      buffer_load_lds16(vrsrc, vd + j * 1024, loff[j], soff);
+      buffer_load_lds16(krsrc, kd + j * 1024, kloff[j], t * C::BN * krs2);
+      buffer_load_lds16(vrsrc, vd + j * 1024, vloff[j], t * C::BN * vrs2);
     }
   };
 
@@ -724,6 +761,12 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
         const int off = kb * 32 * C::CPR * 16 + roff[s];
         sa = mfma_f16(*(const f16x8_t*)(sk + off), qf[s], sa);
         pa = mfma_bf16(*(const bf16x8_t*)(sv + off), of[s], pa);
+      }
+      if constexpr (ALIBI) {  // row i, key j: q.k - (slope / c) |i - j|
+        const float di = (float)(qi - kt - 32 * kb - 4 * hf);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sa[i] = fmaf(fabsf(di - (float)(8 * (i >> 2) + (i & 3))), -slope_raw, sa[i]);
       }
       if (masked) {
         int lo, hi;
@@ -771,7 +814,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   }
 
   if (qi < N) {
-    __bf16* row = (__bf16*)p.dq + base + (size_t)qi * rs;
+    __bf16* row = (__bf16*)p.dq + gbase + (size_t)qi * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
@@ -786,7 +829,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
 
 // ---------------------------------------------------------------- launcher
 
-template <int D>
+template <int D, bool ALIBI>
 static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.N * p.H;
   const long long rpb = 256 / (D / 8);
@@ -797,22 +840,25 @@ static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
   // pair form keeps its state in VGPRs.
   if constexpr (D == 128) {
     p.nblk = (p.N + KvPairCfg<D>::BK - 1) / KvPairCfg<D>::BK;
-    hipLaunchKernelGGL(bwd_dkdv_pair_kernel<D>, dim3(p.B * p.H * p.nblk),
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, ALIBI>), dim3(p.B * p.H * p.nblk),
                        dim3(KvPairCfg<D>::NW * 64), 0, stream, p);
   } else {
     p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(KvCfg<D>::NW * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(p.B * p.H * p.nblk),
+                       dim3(KvCfg<D>::NW * 64), 0, stream, p);
   }
   p.nblk = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64),
+                     0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_backward(BwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
   if (dtype_is_f32) return hipErrorNotSupported;
-  return headdim == 64 ? launch_backward_d<64>(p, stream) : launch_backward_d<128>(p, stream);
+  const bool alibi = p.alibi.slopes != nullptr;
+  if (headdim == 64)
+    return alibi ? launch_backward_d<64, true>(p, stream) : launch_backward_d<64, false>(p, stream);
+  return alibi ? launch_backward_d<128, true>(p, stream) : launch_backward_d<128, false>(p, stream);
 }
 
 }  // namespace fa

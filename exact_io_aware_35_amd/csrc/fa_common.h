@@ -76,6 +76,14 @@ __device__ __forceinline__ void map_block(int nbh, int nblk, int xcd_groups, int
   blk = longest_first ? (nblk - 1 - rank) : rank;
 }
 
+// ALiBi slope of (b, h) in raw score units: the bias -slope |i - j| is added
+// to the scaled score c q.k, so the raw score q.k takes -(slope / c) |i - j|
+// (scale_log2 = c log2 e).
+__device__ __forceinline__ float alibi_raw_slope(const AlibiParams& a, int b, int h,
+                                                 float scale_log2) {
+  return a.slopes[b * a.bstride + h] * (1.4426950408889634f / scale_log2);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return log2f(x); }
 

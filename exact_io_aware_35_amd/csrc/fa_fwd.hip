@@ -66,7 +66,7 @@ struct FwdCfg {
 // operand read by ds_read_b64_tr_b16 (lane i of a 16-lane group receives
 // element (4e + i/4, i%4) of the 16 x 4 block the group addresses, so each
 // lane points at 4 values of one key row and gets 4 keys of one d column).
-template <int D>
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::NBUF * C::TILE];  // [buf][K | V]
@@ -80,12 +80,14 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
   const int N = p.N;
   const int q0 = qblk * C::BM;
   const int kl = key_len(p.mask, b, N);
-  const int rs = p.H * D;                               // elements between sequence positions
-  const size_t base = ((size_t)b * N * p.H + h) * D;    // element (b, 0, h, 0)
+  const int rs = p.rs_q;                                // elements between sequence positions
+  const size_t base = (size_t)b * N * rs + (size_t)h * D;  // element (b, 0, h, 0)
   const __bf16* Q = (const __bf16*)p.q + base;
   const char* Kg = (const char*)((const __bf16*)p.k + base);
   const char* Vg = (const char*)((const __bf16*)p.v + base);
-  __bf16* O = (__bf16*)p.o + base;
+  __bf16* O = (__bf16*)p.o + (size_t)b * N * p.rs_o + (size_t)h * D;
+  float slope_raw = 0.f;
+  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
 
   const int wq0 = q0 + wave * C::QW;                    // first query row of this wave
   int klo, khi;
@@ -180,6 +182,18 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = mfma_bf16(kop, qf[qb][s], sacc[kb][qb]);
       }
+    if constexpr (ALIBI) {  // score of row i, key j: q.k - (slope / c) |i - j|
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const float di = (float)(wq0 + 32 * qb + ln - kt - 4 * hf);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sacc[kb][qb][i] = fmaf(fabsf(di - (float)(32 * kb + 8 * (i >> 2) + (i & 3))), -slope_raw,
+                                   sacc[kb][qb][i]);
+      }
+    }
     if (!block_all_visible(p.mask, kl, wq0, wq1, kt, kt + C::BN - 1)) {
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
@@ -304,7 +318,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     const float l = half_sum(l_part[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qi < N) {
-      __bf16* orow = O + (size_t)qi * rs;
+      __bf16* orow = O + (size_t)qi * p.rs_o;
 #pragma unroll
       for (int d = 0; d < C::DB; ++d)
 #pragma unroll
@@ -325,7 +339,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
 // their natural [key][d] layout in LDS (one element per lane per MFMA, so no
 // transposition is needed). Rows are padded to D + 1 floats so the 32 lanes
 // that read one column hit 32 different banks.
-template <int D>
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
   constexpr int NW = 4, NT = 256, BM = 128, BN = 32, STR = D + 1;
   constexpr int CH = BN * D / 4 / NT;  // float4 chunks per thread per tile
@@ -341,12 +355,14 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
   const int N = p.N;
   const int q0 = qb * BM;
   const int kl = key_len(p.mask, b, N);
-  const size_t rs = (size_t)p.H * D;
-  const size_t base = ((size_t)b * N * p.H + h) * D;
+  const size_t rs = (size_t)p.rs_q;
+  const size_t base = (size_t)b * N * rs + (size_t)h * D;
   const float* Q = (const float*)p.q + base;
   const float* K = (const float*)p.k + base;
   const float* V = (const float*)p.v + base;
-  float* O = (float*)p.o + base;
+  float* O = (float*)p.o + (size_t)b * N * p.rs_o + (size_t)h * D;
+  float slope_raw = 0.f;
+  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
 
   const int qi = q0 + wave * 32 + ln;
   int klo, khi;
@@ -403,6 +419,12 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
       f32x16_t sacc = f32x16_t{};
 #pragma unroll
       for (int s = 0; s < D / 2; ++s) sacc = mfma_f32(sK[buf][ln * STR + 2 * s + hf], qf[s], sacc);
+      if constexpr (ALIBI) {
+        const float di = (float)(qi - kt - 4 * hf);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sacc[i] = fmaf(fabsf(di - (float)(8 * (i >> 2) + (i & 3))), -slope_raw, sacc[i]);
+      }
       if (!block_all_visible(p.mask, kl, wq0, wq1, kt, kt + BN - 1)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -444,7 +466,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
   const float l = half_sum(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (qi < N) {
-    float* orow = O + (size_t)qi * rs;
+    float* orow = O + (size_t)qi * p.rs_o;
 #pragma unroll
     for (int d = 0; d < D / 32; ++d)
 #pragma unroll
@@ -466,15 +488,23 @@ int fwd_block_rows(int dtype_is_f32, int headdim) {
   return headdim == 64 ? FwdCfg<64>::BM : FwdCfg<128>::BM;
 }
 
-hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
+template <bool ALIBI>
+static void launch_forward_a(const FwdParams& p, int headdim, int dtype_is_f32, hipStream_t stream) {
   const dim3 grid(p.B * p.H * p.nqb);
   if (dtype_is_f32) {
-    if (headdim == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(256), 0, stream, p);
+    if (headdim == 64) hipLaunchKernelGGL((fwd_f32_kernel<64, ALIBI>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((fwd_f32_kernel<128, ALIBI>), grid, dim3(256), 0, stream, p);
   } else {
-    if (headdim == 64) hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, dim3(FwdCfg<64>::NW * 64), 0, stream, p);
-    else hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, dim3(FwdCfg<128>::NW * 64), 0, stream, p);
+    if (headdim == 64)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, ALIBI>), grid, dim3(FwdCfg<64>::NW * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, ALIBI>), grid, dim3(FwdCfg<128>::NW * 64), 0, stream, p);
   }
+}
+
+hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
+  if (p.alibi.slopes != nullptr) launch_forward_a<true>(p, headdim, dtype_is_f32, stream);
+  else launch_forward_a<false>(p, headdim, dtype_is_f32, stream);
   return hipGetLastError();
 }
 

@@ -15,6 +15,13 @@ struct MaskParams {
   int wl, wr;
 };
 
+// ALiBi ([notes] docstring): the score of query i and key j gets
+// -slope(b, h) * |i - j|, slope(b, h) = slopes[b * bstride + h].
+struct AlibiParams {
+  const float* slopes;   // null: no bias
+  int bstride;           // 0 (one slope per head) or H (per batch and head)
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -22,7 +29,10 @@ struct FwdParams {
   void* o;
   float* lse;
   MaskParams mask;
+  AlibiParams alibi;
   int B, H, N;
+  int rs_q;              // elements between sequence positions of Q, K and V
+  int rs_o;              // ... of O
   int nqb;               // query blocks per (b, h)
   float scale_log2;      // softmax_scale * log2(e)
   int xcd_groups;        // >0: (b,h) count divisible by 8, remap for XCD locality
@@ -46,7 +56,11 @@ struct BwdParams {
   void* k16;
   void* do16;
   MaskParams mask;
+  AlibiParams alibi;
   int B, H, N;
+  int rs_q;              // elements between sequence positions of Q, K and V
+  int rs_o;              // ... of O and dO
+  int rs_g;              // ... of dQ, dK and dV (the fp16 copies use H * D)
   int nblk;              // blocks per (b, h) along the dimension a kernel tiles
   float scale;           // softmax_scale
   float scale_log2;      // softmax_scale * log2(e)

@@ -19,7 +19,10 @@
  *               (batch, seqlen, nheads, headdim) layout, softmax_scale default
  *               1/sqrt(headdim), causal flag, window_size (left, right) with
  *               keys [i - left, i + right] inclusive and -1 meaning unbounded,
- *               deterministic backward.
+ *               deterministic backward, the packed qkv input (batch, seqlen,
+ *               3, nheads, headdim), and alibi_slopes ((nheads,) or (batch,
+ *               nheads), fp32: -slope * |i - j| added to the score of query i
+ *               and key j).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers to contiguous arrays, 16-byte
@@ -132,6 +135,57 @@ fa_status_t fa_backward(const void* q, const void* k, const void* v,
                         int window_left, int window_right,
                         fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * fa_forward_ex -- fa_forward with the two further options of the
+ * flash_attn_qkvpacked_func docstring ([notes]).
+ *   qkv_packed     : nonzero: q points at ONE tensor [batch][seqlen][3][heads]
+ *                    [headdim] holding Q, K and V (in that order), and k and v
+ *                    must be NULL (else FA_ERR_INVALID_ARG). out stays
+ *                    [batch][seqlen][heads][headdim].
+ *   alibi_slopes   : NULL, or a device fp32 array of slopes, 4-byte aligned;
+ *                    the score of query i and key j in (b, h) becomes
+ *                    softmax_scale * q_i . k_j - slope * |i - j|, with
+ *                    slope = alibi_slopes[b * alibi_batch_stride + h].
+ *   alibi_batch_stride : 0 for (heads,) slopes, heads for (batch, heads);
+ *                    anything else is FA_ERR_INVALID_ARG. Ignored when
+ *                    alibi_slopes is NULL. The slopes are read on the device.
+ * Every other argument, the conventions above and the error behaviour are
+ * those of fa_forward, which equals fa_forward_ex(q, k, v, 0, ..., NULL, 0, ...).
+ * A packed input's (batch, head) slice spans seqlen rows of 3*heads*headdim
+ * elements, which must stay below 2^31 bytes.
+ */
+fa_status_t fa_forward_ex(const void* q, const void* k, const void* v, int qkv_packed,
+                          void* out, float* lse, const int32_t* seqlens_k,
+                          const float* alibi_slopes, int alibi_batch_stride,
+                          int batch, int heads, int seqlen, int headdim,
+                          float softmax_scale, int causal,
+                          int window_left, int window_right,
+                          fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_backward_ex -- fa_backward with the options of fa_forward_ex, which must
+ * match the forward call that produced out and lse.
+ *   qkv_packed : nonzero: q is the packed qkv input as in fa_forward_ex (k, v
+ *                NULL) and dq points at ONE gradient tensor [batch][seqlen][3]
+ *                [heads][headdim] receiving dQ, dK and dV in the same order
+ *                (dk, dv NULL), so no concatenation of gradients is needed
+ *                ([notes]). out and dout stay [batch][seqlen][heads][headdim].
+ *   alibi_slopes, alibi_batch_stride : as in fa_forward_ex. The bias does not
+ *                depend on Q or K, so the gradient formulas are unchanged.
+ * Workspace, conventions and errors are those of fa_backward, which equals
+ * fa_backward_ex(q, k, v, 0, ..., NULL, 0, ...).
+ */
+fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_packed,
+                           const void* out, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv,
+                           const int32_t* seqlens_k,
+                           const float* alibi_slopes, int alibi_batch_stride,
+                           int batch, int heads, int seqlen, int headdim,
+                           float softmax_scale, int causal,
+                           int window_left, int window_right,
+                           fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* Static English name of a status code. Never NULL. */
 const char* fa_status_string(fa_status_t status);

@@ -24,8 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_status_string",
-         "fa_last_error_message"])
+        ["fa_forward", "fa_backward", "fa_forward_ex", "fa_backward_ex",
+         "fa_backward_workspace_size", "fa_status_string", "fa_last_error_message"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -117,3 +117,61 @@ def test_backward_rejects_before_launch(kw, status, needle):
 def test_binding_without_library_fails_loudly(tmp_path):
     with pytest.raises(fb.FaError):
         fb.load_library(str(tmp_path / "missing.so"))
+
+
+def fwd_ex(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, packed=0, out=FAKE, lse=FAKE, seqlens=None, slopes=None,
+             bstride=0, B=2, H=4, N=64, D=128, scale=0.125, causal=0, wl=-1, wr=-1,
+             dtype=fb.FA_DTYPE_BF16)
+    a.update(kw)
+    return lib.fa_forward_ex(a["q"], a["k"], a["v"], a["packed"], a["out"], a["lse"],
+                             a["seqlens"], a["slopes"], a["bstride"], a["B"], a["H"], a["N"],
+                             a["D"], a["scale"], a["causal"], a["wl"], a["wr"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(packed=1), fb.FA_ERR_INVALID_ARG, "k and v must be null"),
+    (dict(packed=1, k=None, v=None, q=None), fb.FA_ERR_INVALID_ARG, "qkv is null"),
+    (dict(packed=1, k=None, v=None, q=FAKE + 8), fb.FA_ERR_INVALID_ARG, "qkv is not 16-byte"),
+    (dict(k=None), fb.FA_ERR_INVALID_ARG, "k is null"),
+    (dict(slopes=FAKE + 2), fb.FA_ERR_INVALID_ARG, "alibi_slopes"),
+    (dict(slopes=FAKE, bstride=3), fb.FA_ERR_INVALID_ARG, "alibi_batch_stride"),
+    # Packed rows are 3x wider: (N + 128) * 3 * H * D * 2 >= 2^31 here, unpacked < 2^31.
+    (dict(packed=1, k=None, v=None, H=64, N=1 << 16, D=128), fb.FA_ERR_UNSUPPORTED, "2^31 bytes"),
+])
+def test_forward_ex_rejects_before_launch(kw, status, needle):
+    lib = fb.load_library()
+    assert fwd_ex(lib, **kw) == status
+    assert needle in lib.fa_last_error_message().decode()
+
+
+def test_packed_slice_limit_is_three_times_wider():
+    lib = fb.load_library()
+    # Same sizes unpacked stay below the limit: rejected later, on a null pointer.
+    assert fwd_ex(lib, H=64, N=1 << 16, D=128, lse=None) == fb.FA_ERR_INVALID_ARG
+    assert "lse is null" in lib.fa_last_error_message().decode()
+
+
+def bwd_ex(lib, **kw):
+    a = dict(q=FAKE, k=None, v=None, packed=1, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=None,
+             dv=None, seqlens=None, slopes=None, bstride=0, B=2, H=3, N=100, D=64, scale=0.125,
+             causal=1, wl=-1, wr=-1, dtype=fb.FA_DTYPE_BF16, ws=FAKE, wsb=1 << 24)
+    a.update(kw)
+    return lib.fa_backward_ex(a["q"], a["k"], a["v"], a["packed"], a["out"], a["lse"],
+                              a["dout"], a["dq"], a["dk"], a["dv"], a["seqlens"], a["slopes"],
+                              a["bstride"], a["B"], a["H"], a["N"], a["D"], a["scale"],
+                              a["causal"], a["wl"], a["wr"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dk=FAKE), fb.FA_ERR_INVALID_ARG, "dk and dv must be null"),
+    (dict(dq=None), fb.FA_ERR_INVALID_ARG, "dqkv is null"),
+    (dict(packed=0, k=FAKE, v=FAKE, dk=FAKE, dv=None), fb.FA_ERR_INVALID_ARG, "dv is null"),
+    (dict(slopes=FAKE, bstride=1), fb.FA_ERR_INVALID_ARG, "alibi_batch_stride"),
+    (dict(ws=None), fb.FA_ERR_WORKSPACE, "workspace"),
+    (dict(dtype=fb.FA_DTYPE_F32), fb.FA_ERR_UNSUPPORTED, "bf16"),
+])
+def test_backward_ex_rejects_before_launch(kw, status, needle):
+    lib = fb.load_library()
+    assert bwd_ex(lib, **kw) == status
+    assert needle in lib.fa_last_error_message().decode()

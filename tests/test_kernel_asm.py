@@ -14,16 +14,17 @@ from exact_io_aware_35_amd import build
 
 
 def kernel_resources(asm):
-    """{kernel name: {field: int}} from the assembler's metadata block."""
+    """{kernel name: {field: int}} from the assembler's metadata: one YAML list
+    entry per kernel under amdhsa.kernels, each starting at "- .agpr_count"."""
+    meta = asm[asm.index("amdhsa.kernels:"):]
     out = {}
-    for m in re.finditer(r"\.name:\s+(_Z\S+)", asm):
-        name = m.group(1)
-        seg = asm[max(0, m.start() - 1500):m.start() + 1500]
+    for entry in re.split(r"\n\s+- \.agpr_count", meta)[1:]:
+        entry = ".agpr_count" + entry
+        name = re.search(r"\.name:\s+(\S+)", entry).group(1)
         fields = {}
         for key in ("vgpr_count", "agpr_count", "vgpr_spill_count", "sgpr_spill_count",
                     "private_segment_fixed_size"):
-            f = re.search(r"\." + key + r":\s+(\d+)", asm[m.start():m.start() + 1500]) or \
-                re.search(r"\." + key + r":\s+(\d+)", seg)
+            f = re.search(r"\." + key + r":\s+(\d+)", entry)
             if f:
                 fields[key] = int(f.group(1))
         out[name] = fields
