@@ -217,8 +217,9 @@ def cpu_baseline(w, seconds):
                       f"query rows each, fp64 numpy; {dt:.1f} s"}
 
 
-def run_workload(w, steps, warmup, backward=False):
-    """(fwd ms, bwd ms or None) for workload w on cuda:0."""
+def run_workload(w, steps, warmup, backward=False, variant=None):
+    """(fwd ms, bwd ms or None) for workload w on cuda:0. variant: None, "alibi"
+    (the usual geometric slopes per head) or "qkvpacked" (one packed input)."""
     import torch
     import exact_io_aware_35_amd as fa
     from exact_io_aware_35_amd.inputs import make_inputs
@@ -229,15 +230,28 @@ def run_workload(w, steps, warmup, backward=False):
     out = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.seqlen), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, window=w.window, softmax_scale=w.softmax_scale, seqlens_k=sk)
-    fwd = fa.prepare_forward(q, k, v, out, lse, **kw)
+    if variant is None:
+        fwd = fa.prepare_forward(q, k, v, out, lse, **kw)
+    elif variant == "alibi":
+        kw["alibi_slopes"] = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.heads) for h in range(w.heads)],
+                                          dtype=torch.float32, device=dev)
+        fwd = lambda: fa.forward(q, k, v, out=out, lse=lse, **kw)
+    else:
+        qkv = torch.stack([q, k, v], dim=2).contiguous()
+        fwd = lambda: fa.forward_qkvpacked(qkv, out=out, lse=lse, **kw)
     t_f = time_gpu(fwd, steps, warmup)
     t_b = None
     if backward:
         do = d["dout"].to(dev) if d["dout"] is not None else torch.randn_like(q)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(fa.workspace_size(w.batch, w.heads, w.seqlen, w.headdim),
                          dtype=torch.uint8, device=dev)
-        bwd = lambda: fa.backward(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        if variant == "qkvpacked":
+            dqkv = torch.empty_like(qkv)
+            bwd = lambda: fa.backward_qkvpacked(qkv, out, lse, do, dqkv=dqkv, workspace=ws, **kw)
+        else:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            bwd = lambda: fa.backward(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                      **kw)
         t_b = time_gpu(bwd, steps, warmup)
     return t_f, t_b, (fwd, q)
 
@@ -335,6 +349,12 @@ def main():
             rec = {"workload": name, "fwd_ms": round(tf, 4), "fwd_tflops": round(ff / tf / 1e9, 2)}
             if tb is not None:
                 rec.update(bwd_ms=round(tb, 4), bwd_tflops=round(2.5 * ff / tb / 1e9, 2))
+            print("extra: " + json.dumps(rec), file=sys.stderr, flush=True)
+        for variant in ("alibi", "qkvpacked"):
+            tf, tb, _ = run_workload(w, 20, 3, backward=True, variant=variant)
+            rec = {"workload": w.name, "variant": variant, "fwd_ms": round(tf, 4),
+                   "fwd_tflops": round(flops / tf / 1e9, 2), "bwd_ms": round(tb, 4),
+                   "bwd_tflops": round(2.5 * flops / tb / 1e9, 2)}
             print("extra: " + json.dumps(rec), file=sys.stderr, flush=True)
     if args.copy_mib:
         plain_copy(args.copy_mib)
