@@ -20,9 +20,9 @@
  *               1/sqrt(headdim), causal flag, window_size (left, right) with
  *               keys [i - left, i + right] inclusive and -1 meaning unbounded,
  *               deterministic backward, the packed qkv input (batch, seqlen,
- *               3, nheads, headdim), and alibi_slopes ((nheads,) or (batch,
- *               nheads), fp32: -slope * |i - j| added to the score of query i
- *               and key j).
+ *               3, nheads, headdim), and ALiBi slopes (fp32, per head or per
+ *               batch and head; the score of query i and key j is lowered by
+ *               slope times |i - j|).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers to contiguous arrays, 16-byte

@@ -26,10 +26,10 @@ Readings where the pages are silent or wrong:
   beside it says a query sees only keys at or before it).
 * Key padding: keys j >= L_b of sequence b are invisible to every query row of
   that sequence; query rows are all still computed.
-* ALiBi ([notes] docstring, ``alibi_slopes``: (nheads,) or (batch, nheads),
-  fp32; a bias -slope * |i - j| is added to the attention score of query i
-  and key j): the bias is added to the scaled score, S = c q.k - slope |i - j|,
-  before masking and softmax. It does not depend on Q or K, so the backward's
+* ALiBi ([notes] docstring, the ``alibi_slopes`` argument: one fp32 slope
+  per head, or per batch and head, lowering the score of query i and key j
+  by slope times their distance): the bias joins the scaled score,
+  S = c q.k - slope |i - j|, before masking and softmax. It does not depend on Q or K, so the backward's
   formulas are unchanged (dS is the gradient of the biased score, and the
   biased score's derivative in q.k is still c).
 
