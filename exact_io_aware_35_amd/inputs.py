@@ -9,6 +9,11 @@ Recipe (the same for every caller): one CPU ``torch.Generator`` seeded with
 the per-sequence key lengths L_b = randint(lo, hi + 1); then, if the case is
 sampled, the query rows; finally cast Q, K, V, dO to the working dtype with
 round-to-nearest-even (``Tensor.to``). dO is drawn with std 1 in every case.
+
+fp8 cases draw Q, K, V the same way, then store each as e4m3 bytes of
+x / descale (``Tensor.to(torch.float8_e4m3fn)``, round to nearest even)
+with descale = std / 32, a power of two: values up to ~14 std stay inside
+e4m3's range (448), and the dequantised value is e4m3(byte) * descale.
 """
 
 from __future__ import annotations
@@ -27,7 +32,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "fp8" (e4m3 bytes + a factor per tensor)
     batch: int
     heads: int
     seqlen: int
@@ -63,6 +68,9 @@ WORKLOADS = {
         "fwd_bf16_b1h16n65536d128_window4096", "bf16", 1, 16, 65536, 128,
         causal=True, window=(4096, 0), sample_rows=256,
         extra_rows=(0, 1, 4095, 4096, 4097, 65535)),
+    "fwd_fp8_b2h8n4096d128": Workload(
+        "fwd_fp8_b2h8n4096d128", "fp8", 2, 8, 4096, 128, sample_rows=256,
+        extra_rows=(0, 1, 4095)),
 }
 
 METRIC_WORKLOAD = "fwd_bf16_b2h8n4096d128"
@@ -78,13 +86,21 @@ def make_inputs(w: Workload, seed: int = 0):
     """
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     shape = (w.batch, w.seqlen, w.heads, w.headdim)
-    dt = TORCH_DTYPE[w.dtype]
+    fp8 = w.dtype == "fp8"
+    dt = None if fp8 else TORCH_DTYPE[w.dtype]
     out = {}
+    if fp8:
+        out["descale"] = {}
     for name in ("q", "k", "v"):
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         if w.std != 1.0:
             x.mul_(w.std)
-        out[name] = x.to(dt)
+        if fp8:
+            descale = w.std / 32.0
+            out[name] = x.div_(descale).to(torch.float8_e4m3fn).view(torch.uint8)
+            out["descale"][name] = descale
+        else:
+            out[name] = x.to(dt)
         del x
     out["dout"] = None
     if w.backward:
