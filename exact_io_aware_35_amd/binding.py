@@ -38,6 +38,8 @@ SIGNATURES = [
                            _P]),
     ("fa_backward_ex", _I, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                             _F, _I, _I, _I, _I, _P, _SZ, _P]),
+    ("fa_forward_fp8", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _F, _I, _I, _I,
+                            _P]),
     ("fa_status_string", ctypes.c_char_p, [_I]),
     ("fa_last_error_message", ctypes.c_char_p, []),
 ]
@@ -159,6 +161,38 @@ def forward_qkvpacked(qkv, causal=False, window=(-1, -1), softmax_scale=None, se
     B, N, _, H, D = qkv.shape
     return _forward(qkv, None, None, True, (B, N, H, D), causal, window, softmax_scale,
                     seqlens_k, alibi_slopes, out, lse, stream)
+
+
+def forward_fp8(q8, k8, v8, descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=False,
+                window=(-1, -1), softmax_scale=None, seqlens_k=None, out=None, lse=None,
+                stream=None):
+    """O (bf16), LSE of attention over fp8 inputs (fa_forward_fp8).
+
+    q8, k8, v8: e4m3 bytes [batch, seqlen, heads, headdim] on the device, as
+    torch.uint8 or torch.float8_e4m3fn; element x of q8 stands for
+    e4m3(x) * descale_q (likewise k8, v8). Returns (out bf16, lse fp32).
+    """
+    import torch
+    if k8.shape != q8.shape or v8.shape != q8.shape:
+        raise FaError(FA_ERR_INVALID_ARG, "q8, k8, v8 must have the same shape")
+    for t, name in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.element_size() != 1:
+            raise FaError(FA_ERR_INVALID_ARG, f"{name} must hold one byte per element")
+    lib = load_library()
+    B, N, H, D = q8.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    st = lib.fa_forward_fp8(_dev_ptr(q8, "q8"), _dev_ptr(k8, "k8"), _dev_ptr(v8, "v8"),
+                            _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                            _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale,
+                            float(descale_q), float(descale_k), float(descale_v),
+                            int(bool(causal)), int(window[0]), int(window[1]),
+                            _stream_handle(stream, q8.device))
+    _check(lib, st)
+    return out, lse
 
 
 class PreparedCall:

@@ -28,7 +28,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shared size/mask/scale checks. On success fills the folded window bounds.
 fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float scale,
                          int causal, int wl, int wr, fa_dtype_t dtype, int* wl_eff,
-                         int* wr_eff, int row_mult = 1) {
+                         int* wr_eff, int row_mult = 1, int elem_bytes = 0) {
   if (batch < 1 || heads < 1 || seqlen < 1)
     return fail(FA_ERR_INVALID_ARG, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)",
                 batch, heads, seqlen);
@@ -42,8 +42,9 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
     return fail(FA_ERR_UNSUPPORTED, "headdim %d is not supported (64 or 128)", headdim);
   // Kernels address one (batch, head) slice with 32-bit byte offsets (buffer
   // loads take a 32-bit offset); one key tile of slack covers the prefetch.
-  // row_mult is 3 for a packed (batch, seqlen, 3, heads, headdim) input.
-  const long long esize = dtype == FA_DTYPE_F32 ? 4 : 2;
+  // row_mult is 3 for a packed (batch, seqlen, 3, heads, headdim) input;
+  // elem_bytes, when set, overrides the element size of dtype.
+  const long long esize = elem_bytes > 0 ? elem_bytes : (dtype == FA_DTYPE_F32 ? 4 : 2);
   if (((long long)seqlen + 128) * row_mult * heads * headdim * esize >= (1LL << 31))
     return fail(FA_ERR_UNSUPPORTED, "a (batch, head) slice of seqlen rows of the input must "
                 "span less than 2^31 bytes");
@@ -196,6 +197,53 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v, void* out, f
                        fa_dtype_t dtype, hipStream_t stream) {
   return fa_forward_ex(q, k, v, 0, out, lse, seqlens_k, nullptr, 0, batch, heads, seqlen,
                        headdim, softmax_scale, causal, window_left, window_right, dtype, stream);
+}
+
+fa_status_t fa_forward_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* seqlens_k, int batch, int heads, int seqlen,
+                           int headdim, float softmax_scale, float descale_q, float descale_k,
+                           float descale_v, int causal, int window_left, int window_right,
+                           hipStream_t stream) {
+  g_msg[0] = '\0';
+  int wl, wr;
+  fa_status_t s = check_common(batch, heads, seqlen, headdim, softmax_scale, causal,
+                               window_left, window_right, FA_DTYPE_BF16, &wl, &wr, 1, 1);
+  if (s != FA_OK) return s;
+  const float ds[3] = {descale_q, descale_k, descale_v};
+  const char* const dnames[3] = {"descale_q", "descale_k", "descale_v"};
+  for (int i = 0; i < 3; ++i)
+    if (!std::isfinite(ds[i]) || !(ds[i] > 0.f))
+      return fail(FA_ERR_INVALID_ARG, "%s must be finite and > 0", dnames[i]);
+  const float scale_log2 = softmax_scale * descale_q * descale_k * 1.4426950408889634f;
+  if (!std::isfinite(scale_log2) || !(scale_log2 > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "softmax_scale * descale_q * descale_k is not a finite "
+                "positive fp32 value");
+  const void* ptrs[] = {q, k, v};
+  for (int i = 0; i < 3; ++i)
+    if ((s = check_ptr(ptrs[i], kQkvNames[i + 1])) != FA_OK) return s;
+  if ((s = check_ptr(out, "out")) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse")) != FA_OK) return s;
+  if (seqlens_k != nullptr && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+  p.mask.seqlens_k = seqlens_k;
+  p.mask.wl = wl;
+  p.mask.wr = wr;
+  p.B = batch; p.H = heads; p.N = seqlen;
+  p.rs_q = heads * headdim;  // bytes: one byte per element
+  p.rs_o = heads * headdim;
+  const int bm = fa::fwd_fp8_block_rows(headdim);
+  p.nqb = (seqlen + bm - 1) / bm;
+  p.scale_log2 = scale_log2;
+  p.xcd_groups = (batch * heads) % 8 == 0 ? 1 : 0;
+  p.longest_first = wr >= 0 ? 1 : 0;
+  if ((long long)batch * heads * p.nqb >= (1LL << 31))
+    return fail(FA_ERR_INVALID_ARG, "grid too large");
+  hipError_t e = fa::launch_forward_fp8(p, descale_v, headdim, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fp8 forward launch: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,

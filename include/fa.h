@@ -187,6 +187,34 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
                            fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * fa_forward_fp8 -- the forward of fa_forward over fp8 inputs. The pages list
+ * an FP8 forward among the additions of FlashAttention-3 ([interview] section
+ * "v1 → v2 → v3 演进", the v3 row; [wiki] section "典型例子", the paragraph on
+ * the official repository); here it runs on the gfx950 fp8 matrix cores.
+ *   q, k, v   in : [batch][seqlen][heads][headdim], one byte per element in
+ *                  the OCP e4m3 format (bias 7, 3 mantissa bits, subnormals,
+ *                  0x7f / 0xff NaN, no infinities)
+ *   descale_q, descale_k, descale_v : fp32 factors, finite and > 0; element x
+ *                  of Q stands for e4m3(x) * descale_q, and likewise for K, V
+ *   out       out: [batch][seqlen][heads][headdim], bfloat16
+ *   lse       out: [batch][heads][seqlen], fp32, natural log
+ * The result is the attention of fa_forward over the dequantised inputs, with
+ * one further rounding: the probabilities are rounded to e4m3 (nearest even)
+ * before the product with V, at a scale where the row's largest probability
+ * lies in [2^8, 2^8.8]. The LSE is computed from the unrounded probabilities.
+ * Inputs must not hold NaN. seqlens_k, softmax_scale, causal, the window, the
+ * conventions and the error behaviour are those of fa_forward (dtype is fixed
+ * here); a (batch, head) slice of seqlen + 128 rows must span less than 2^31
+ * bytes.
+ */
+fa_status_t fa_forward_fp8(const void* q, const void* k, const void* v,
+                           void* out, float* lse, const int32_t* seqlens_k,
+                           int batch, int heads, int seqlen, int headdim,
+                           float softmax_scale, float descale_q, float descale_k,
+                           float descale_v, int causal,
+                           int window_left, int window_right, hipStream_t stream);
+
 /* Static English name of a status code. Never NULL. */
 const char* fa_status_string(fa_status_t status);
 

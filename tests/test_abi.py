@@ -19,12 +19,12 @@ pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_backward", "fa_forward_ex", "fa_backward_ex",
+        ["fa_forward", "fa_backward", "fa_forward_ex", "fa_backward_ex", "fa_forward_fp8",
          "fa_backward_workspace_size", "fa_status_string", "fa_last_error_message"])
 
 
@@ -175,3 +175,44 @@ def test_backward_ex_rejects_before_launch(kw, status, needle):
     lib = fb.load_library()
     assert bwd_ex(lib, **kw) == status
     assert needle in lib.fa_last_error_message().decode()
+
+
+def fwd_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, seqlens=None, B=2, H=4, N=64, D=128,
+             scale=0.125, dq=0.5, dk=0.25, dv=2.0, causal=0, wl=-1, wr=-1)
+    a.update(kw)
+    return lib.fa_forward_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["seqlens"], a["B"],
+                              a["H"], a["N"], a["D"], a["scale"], a["dq"], a["dk"], a["dv"],
+                              a["causal"], a["wl"], a["wr"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dq=0.0), fb.FA_ERR_INVALID_ARG, "descale_q"),
+    (dict(dk=float("nan")), fb.FA_ERR_INVALID_ARG, "descale_k"),
+    (dict(dv=float("inf")), fb.FA_ERR_INVALID_ARG, "descale_v"),
+    (dict(dv=-1.0), fb.FA_ERR_INVALID_ARG, "descale_v"),
+    (dict(dq=1e30, dk=1e30), fb.FA_ERR_INVALID_ARG, "finite positive"),
+    (dict(scale=0.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
+    (dict(B=0), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(wl=-2), fb.FA_ERR_INVALID_ARG, "window"),
+    (dict(q=None), fb.FA_ERR_INVALID_ARG, "q is null"),
+    (dict(v=FAKE + 8), fb.FA_ERR_INVALID_ARG, "v is not 16-byte aligned"),
+    (dict(out=None), fb.FA_ERR_INVALID_ARG, "out is null"),
+    (dict(lse=FAKE + 4), fb.FA_ERR_INVALID_ARG, "lse is not 16-byte aligned"),
+    (dict(seqlens=FAKE + 2), fb.FA_ERR_INVALID_ARG, "seqlens_k"),
+    # One byte per element: (N + 128) * H * D >= 2^31 needs H = 128 at N = 2^17.
+    (dict(H=128, N=1 << 17, D=128), fb.FA_ERR_UNSUPPORTED, "2^31 bytes"),
+])
+def test_forward_fp8_rejects_before_launch(kw, status, needle):
+    lib = fb.load_library()
+    assert fwd_fp8(lib, **kw) == status
+    assert needle in lib.fa_last_error_message().decode()
+
+
+def test_fp8_slice_limit_counts_one_byte_per_element():
+    lib = fb.load_library()
+    # 2-byte elements would exceed 2^31 here; one byte does not: the call gets
+    # past the size check and stops at the null lse.
+    assert fwd_fp8(lib, H=64, N=1 << 17, D=128, lse=None) == fb.FA_ERR_INVALID_ARG
+    assert "lse is null" in lib.fa_last_error_message().decode()

@@ -31,7 +31,7 @@ def kernel_resources(asm):
     return out
 
 
-@pytest.fixture(scope="module", params=["fa_fwd.hip", "fa_bwd.hip"])
+@pytest.fixture(scope="module", params=["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip"])
 def resources(request, tmp_path_factory):
     out = tmp_path_factory.mktemp("asm") / (request.param + ".s")
     return kernel_resources(open(build.device_asm(request.param, str(out))).read())

@@ -1,0 +1,165 @@
+"""GPU parity of the fp8 (e4m3) forward through the C ABI (fa_forward_fp8)
+against the fp64 oracle of oracle/fp8.py on identical seeded inputs.
+
+Tolerance. The oracle is exact attention over the dequantised inputs. The
+kernel differs from it by the e4m3 rounding of P, bounded per element by
+B = 2^-4 sum_j w_j |v_j| + 2^-18 sum_j |v_j| (derived in oracle/fp8.py), and
+by roundings that are small beside it: the bf16 output (2^-8 of the value),
+the fp32 exponential and scores (relative 1e-3 of the weights, generously),
+and fp32 sums over N keys (gamma_N = N 2^-24 of sum_j w_j |v_j| <= 16 B and of
+|O|). Hence, per element,
+
+    |O - O_ref| <= B (1 + 2^-8 + 16 (gamma_N + 1e-3)) + (2^-8 + gamma_N) |O_ref| + 1e-6.
+
+The LSE sees no fp8 rounding (l sums the unrounded P; the scores are exact
+sums of exact products up to fp32 rounding): 1e-3, as for bf16, plus the fp32
+dot-product bound for large scores, gamma_D c sum_d |q_d k_d| + 4 u max |s|
+(u = 2^-24; the standard bound for a length-D fp32 sum, and a few roundings of
+the scale and the LSE itself), which matters for the std-4 case. Inputs with
+std 2 make attention peaked (score std ~4), so O follows single keys and a
+wrong key order in either product would exceed B by far; std-1 inputs keep
+attention diffuse and check that B holds where many roundings add up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_35_amd import forward_fp8
+from exact_io_aware_35_amd.inputs import WORKLOADS, make_case, make_inputs
+from oracle.fp8 import (attention_forward_fp8, attention_forward_fp8_rows, dequantise,
+                        fp8_output_bound)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LSE_TOL = 1e-3
+
+
+def run(d, causal=False, window=(-1, -1), scale=None):
+    ds = d["descale"]
+    sk = None if d["seqlens_k"] is None else d["seqlens_k"].to(DEV)
+    o, lse = forward_fp8(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), ds["q"], ds["k"], ds["v"],
+                         causal=causal, window=window, softmax_scale=scale, seqlens_k=sk)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_args(d):
+    ds = d["descale"]
+    return (d["q"].numpy(), d["k"].numpy(), d["v"].numpy(), ds["q"], ds["k"], ds["v"])
+
+
+def assert_fp8_close(o, ro, bound, n_keys, what="O"):
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    gamma = n_keys * 2.0 ** -24
+    tol = bound * (1 + 2.0 ** -8 + 16 * (gamma + 1e-3)) + (2.0 ** -8 + gamma) * np.abs(ro) + 1e-6
+    err = np.abs(o - ro)
+    worst = float((err / tol).max())
+    assert (err <= tol).all(), f"{what}: error reaches {worst:.3g} of the fp8 bound"
+    return worst
+
+
+def assert_lse(got, want, tol=LSE_TOL):
+    inf_w, inf_g = np.isneginf(want), np.isneginf(got)
+    assert (inf_w == inf_g).all(), "lse: -inf rows differ"
+    fin = ~inf_w
+    err = np.abs(got[fin] - want[fin]).max() if fin.any() else 0.0
+    assert err <= tol, f"lse: max abs err {err:.3g} > {tol}"
+
+
+def score_rounding(d, scale):
+    """gamma_D c max sum_d |q_d k_d| + 4 u c max |q . k| over all (b, h, i, j)."""
+    q, k, _ = dequantise(*oracle_args(d))
+    D = q.shape[-1]
+    c = 1.0 / np.sqrt(D) if scale is None else scale
+    u = 2.0 ** -24
+    sabs = smax = 0.0
+    for b in range(q.shape[0]):
+        for h in range(q.shape[2]):
+            sabs = max(sabs, float((np.abs(q[b, :, h]) @ np.abs(k[b, :, h]).T).max()))
+            smax = max(smax, float(np.abs(q[b, :, h] @ k[b, :, h].T).max()))
+    return D * u / (1 - D * u) * c * sabs + 4 * u * c * smax
+
+
+def check(d, causal=False, window=(-1, -1), scale=None):
+    o, lse = run(d, causal, window, scale)
+    sk = None if d["seqlens_k"] is None else d["seqlens_k"].numpy()
+    mask = dict(softmax_scale=scale, causal=causal, window=window, seqlens_k=sk)
+    ro, rl = attention_forward_fp8(*oracle_args(d), **mask)
+    bnd = fp8_output_bound(*oracle_args(d), **mask)
+    worst = assert_fp8_close(o, ro, bnd, d["q"].shape[1])
+    assert_lse(lse, rl, LSE_TOL + score_rounding(d, scale))
+    return worst
+
+
+MASKS = [
+    dict(),
+    dict(causal=True),
+    dict(window=(37, 5)),
+    dict(window=(0, 0)),
+    dict(causal=True, window=(50, 0)),
+    dict(window=(-1, 70)),
+]
+
+
+@pytest.mark.parametrize("std", [1.0, 2.0])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", MASKS, ids=lambda m: "-".join(f"{k}{v}" for k, v in m.items()) or "none")
+def test_fp8_forward_small(std, D, mask):
+    d = make_case(2, 300, 3, D, dtype="fp8", std=std, seed=11)
+    check(d, **mask)
+
+
+@pytest.mark.parametrize("seqlens,mask", [
+    ([300, 17], dict()),
+    ([300, 17], dict(causal=True)),
+    ([0, 129], dict()),
+    ([5, 300], dict(window=(0, 0))),
+    ([64, 200], dict(causal=True, window=(20, 0))),
+])
+def test_fp8_forward_key_padding(seqlens, mask):
+    d = make_case(2, 300, 2, 128, dtype="fp8", std=2.0, seed=12, seqlens_k=seqlens)
+    check(d, **mask)
+
+
+@pytest.mark.parametrize("N", [1, 7, 63, 64, 65, 128, 129, 257])
+def test_fp8_forward_lengths(N):
+    d = make_case(1, N, 2, 128, dtype="fp8", std=2.0, seed=13)
+    check(d)
+    check(d, causal=True)
+
+
+def test_fp8_forward_scales():
+    """Descale factors other than the inputs' own (the kernel folds dq dk into
+    the exponent's scale and dv into the epilogue) and a non-default softmax
+    scale: all three factors move the result the way the oracle says."""
+    d = make_case(1, 200, 2, 64, dtype="fp8", std=1.0, seed=14)
+    d["descale"] = {"q": 0.09, "k": 0.02, "v": 3.0}
+    check(d)
+    check(d, causal=True, scale=0.3)
+
+
+def test_fp8_peaked_rows_follow_one_key():
+    """With std-4 inputs most rows put nearly all weight on one key: O is then
+    that key's V row to within the bound, which only a correct pairing of
+    scores, probabilities and V rows gives."""
+    d = make_case(1, 256, 2, 128, dtype="fp8", std=4.0, seed=15)
+    worst = check(d)
+    assert worst <= 1.0
+
+
+def test_fp8_b2h8n4096d128_sampled_rows():
+    """The full-size shape, launched as the benchmark launches it; 259 query
+    rows per head checked against the oracle."""
+    w = WORKLOADS["fwd_fp8_b2h8n4096d128"]
+    d = make_inputs(w, 0)
+    o, lse = run(d, w.causal, w.window)
+    rows = d["rows"].numpy()
+    args = oracle_args(d)
+    ro, rl = attention_forward_fp8_rows(*args, rows=rows, softmax_scale=w.softmax_scale)
+    bnd = fp8_output_bound(*args, softmax_scale=w.softmax_scale, rows=rows)
+    got_o = np.stack([o[:, rows[h], h, :] for h in range(w.heads)], axis=1)
+    got_l = np.stack([lse[:, h, rows[h]] for h in range(w.heads)], axis=1)
+    assert_fp8_close(got_o, ro, bnd, w.seqlen)
+    assert_lse(got_l, rl)
