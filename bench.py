@@ -33,7 +33,7 @@ METRIC_WORKLOAD_NAME = "fwd_bf16_b2h8n4096d128"
 STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -- python bench.py "
              "--workload {workload} --steps 200 --warmup 50 --no-cpu-baseline")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_b2h8n4096d128.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_35_amd", "csrc", f)
@@ -56,8 +56,10 @@ def fwd_flops(w, causal=None):
 
 def algorithmic_bytes(w):
     """Compulsory HBM bytes of one forward: read Q, K, V; write O and LSE."""
-    esz = 2 if w.dtype == "bf16" else 4
     n = w.batch * w.seqlen * w.heads * w.headdim
+    if w.dtype == "fp8":  # e4m3 inputs, bf16 output
+        return 3 * n + 2 * n + w.batch * w.heads * w.seqlen * 4
+    esz = 2 if w.dtype == "bf16" else 4
     return 4 * n * esz + w.batch * w.heads * w.seqlen * 4
 
 
@@ -194,8 +196,15 @@ def cpu_baseline(w, seconds):
     import threadpoolctl
     from exact_io_aware_35_amd.inputs import make_inputs
     from oracle import attention_forward
+    from oracle.fp8 import attention_forward_fp8
     d = make_inputs(w, 0)
-    q, k, v = (d[x].float().numpy() for x in ("q", "k", "v"))
+    if w.dtype == "fp8":
+        q, k, v = (d[x].numpy() for x in ("q", "k", "v"))
+        ds = d["descale"]
+        attention_forward = lambda q_, k_, v_, *a: attention_forward_fp8(  # noqa: E731
+            q_, k_, v_, ds["q"], ds["k"], ds["v"], *a)
+    else:
+        q, k, v = (d[x].float().numpy() for x in ("q", "k", "v"))
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     done, t0 = 0, time.perf_counter()
@@ -227,9 +236,13 @@ def run_workload(w, steps, warmup, backward=False, variant=None):
     dev = torch.device("cuda:0")
     q, k, v = (d[x].to(dev) for x in ("q", "k", "v"))
     sk = d["seqlens_k"].to(dev) if d["seqlens_k"] is not None else None
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "fp8" else q.dtype, device=dev)
     lse = torch.empty((w.batch, w.heads, w.seqlen), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, window=w.window, softmax_scale=w.softmax_scale, seqlens_k=sk)
+    if w.dtype == "fp8":
+        ds = d["descale"]
+        fwd = fa.prepare_forward_fp8(q, k, v, out, lse, ds["q"], ds["k"], ds["v"], **kw)
+        return time_gpu(fwd, steps, warmup), None, (fwd, q)
     if variant is None:
         fwd = fa.prepare_forward(q, k, v, out, lse, **kw)
     elif variant == "alibi":
@@ -331,7 +344,9 @@ def main():
         "frac_of_mfma_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
-                     "traffic": traffic, "kernel": "fwd_bf16_kernel",
+                     "traffic": traffic if w.name == METRIC_WORKLOAD_NAME else None,
+                     "kernel": {"bf16": "fwd_bf16_kernel", "f32": "fwd_f32_kernel",
+                                "fp8": "fwd_fp8_kernel"}[w.dtype],
                      "launch_ms_mean": round(mean_ms, 5), "launch_ms_median": round(med_ms, 5),
                      "algorithmic_bytes": algorithmic_bytes(w)},
         "cpu_baseline": None,

@@ -229,6 +229,21 @@ def prepare_forward(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_sc
     return call
 
 
+def prepare_forward_fp8(q8, k8, v8, out, lse, descale_q, descale_k, descale_v, causal=False,
+                        window=(-1, -1), softmax_scale=None, seqlens_k=None, stream=None):
+    """forward_fp8() with every argument marshalled once; returns a callable."""
+    lib = load_library()
+    B, N, H, D = q8.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    args = (_dev_ptr(q8, "q8"), _dev_ptr(k8, "k8"), _dev_ptr(v8, "v8"), _dev_ptr(out, "out"),
+            _dev_ptr(lse, "lse"), _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D, scale,
+            float(descale_q), float(descale_k), float(descale_v), int(bool(causal)),
+            int(window[0]), int(window[1]), _stream_handle(stream, q8.device))
+    call = PreparedCall(lib.fa_forward_fp8, args, (q8, k8, v8, out, lse, seqlens_k))
+    call()  # surfaces argument errors now
+    return call
+
+
 def workspace_size(batch, heads, seqlen, headdim, dtype_code=FA_DTYPE_BF16):
     return int(load_library().fa_backward_workspace_size(batch, heads, seqlen, headdim, dtype_code))
 

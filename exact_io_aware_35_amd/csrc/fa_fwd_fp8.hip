@@ -44,9 +44,9 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 
-template <int D>
+template <int D, int NW_ = (D == 128 ? 8 : 4)>
 struct Fp8Cfg {
-  static constexpr int NW = D == 128 ? 8 : 4;  // waves per work-group
+  static constexpr int NW = NW_;               // waves per work-group
   static constexpr int QW = 32;                // query rows per wave
   static constexpr int BM = NW * QW;           // query rows per work-group
   static constexpr int BN = 64;                // keys per tile
@@ -54,7 +54,8 @@ struct Fp8Cfg {
   static constexpr int TILE = BN * D;          // bytes of one K or V tile
   static constexpr int DS = D / 64;            // 64-deep steps of the S product
   static constexpr int DB = D / 32;            // 32-wide d blocks of O
-  static_assert(TILE == NW * 1024, "one 1 KiB direct-to-LDS load per wave per tile");
+  static constexpr int LPW = TILE / 1024 / NW; // 1 KiB direct-to-LDS loads per wave per matrix
+  static_assert(LPW >= 1 && TILE == LPW * NW * 1024, "tile must split into 1 KiB loads");
 };
 
 // LDS tiles: [64 keys][D bytes], 16-byte chunks XOR-swizzled per row. With a
@@ -92,9 +93,15 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
+// Four waves (128 query rows) per work-group at both head dimensions: with
+// ~150 VGPRs three such work-groups fit on a CU, which measured faster than
+// eight-wave groups (two waves per SIMD) at D = 128.
 template <int D>
-__global__ void __launch_bounds__(Fp8Cfg<D>::NW * 64) fwd_fp8_kernel(FwdParams p, float v_descale) {
-  using C = Fp8Cfg<D>;
+using Fp8Shape = Fp8Cfg<D, 4>;
+
+template <int D>
+__global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) fwd_fp8_kernel(FwdParams p, float v_descale) {
+  using C = Fp8Shape<D>;
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];  // [buf][K | V]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -132,23 +139,30 @@ __global__ void __launch_bounds__(Fp8Cfg<D>::NW * 64) fwd_fp8_kernel(FwdParams p
     }
   }
 
-  // Direct-to-LDS copies: lane u = 64 wave + lane fills LDS chunk u of a tile
-  // (row u / CPR, position u % CPR) with the global chunk that the row's
-  // swizzle puts there. Rows at or past N read as zero.
+  // Direct-to-LDS copies: load j of a wave fills LDS chunk
+  // u = 64 (LPW wave + j) + lane of a tile (row u / CPR, position u % CPR)
+  // with the global chunk that the row's swizzle puts there. Rows at or past
+  // N read as zero.
   const int nbytes = (N - 1) * rs + D;
   const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(Kg, nbytes);
   const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(Vg, nbytes);
-  int kload, vload;
-  {
-    const int u = wave * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
-    kload = row * rs + (pos ^ swz_k<D>(row)) * 16;
-    vload = row * rs + (pos ^ swz_v<D>(row)) * 16;
+  int kload[C::LPW], vload[C::LPW];
+#pragma unroll
+  for (int j = 0; j < C::LPW; ++j) {
+    const int u = (wave * C::LPW + j) * 64 + lane, row = u / C::CPR, pos = u % C::CPR;
+    kload[j] = row * rs + (pos ^ swz_k<D>(row)) * 16;
+    vload[j] = row * rs + (pos ^ swz_v<D>(row)) * 16;
   }
   auto issue_tile = [&](int t, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int soff = t * C::BN * rs;
-    buffer_load_lds16(krsrc, smem + (2 * buf) * C::TILE + wave * 1024, kload, soff);
-    buffer_load_lds16(vrsrc, smem + (2 * buf + 1) * C::TILE + wave * 1024, vload, soff);
+    char* kd = smem + (2 * buf) * C::TILE + wave * C::LPW * 1024;
+    char* vd = smem + (2 * buf + 1) * C::TILE + wave * C::LPW * 1024;
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) {
+      buffer_load_lds16(krsrc, kd + j * 1024, kload[j], soff);
+      buffer_load_lds16(vrsrc, vd + j * 1024, vload[j], soff);
+    }
   };
 
   // LDS read offsets. S operand of block kb, step s: key row
@@ -302,14 +316,14 @@ __global__ void __launch_bounds__(Fp8Cfg<D>::NW * 64) fwd_fp8_kernel(FwdParams p
   }
 }
 
-int fwd_fp8_block_rows(int headdim) { return headdim == 64 ? Fp8Cfg<64>::BM : Fp8Cfg<128>::BM; }
+int fwd_fp8_block_rows(int headdim) { return headdim == 64 ? Fp8Shape<64>::BM : Fp8Shape<128>::BM; }
 
 hipError_t launch_forward_fp8(FwdParams p, float v_descale, int headdim, hipStream_t stream) {
   const dim3 grid(p.B * p.H * p.nqb);
   if (headdim == 64)
-    hipLaunchKernelGGL((fwd_fp8_kernel<64>), grid, dim3(Fp8Cfg<64>::NW * 64), 0, stream, p, v_descale);
+    hipLaunchKernelGGL((fwd_fp8_kernel<64>), grid, dim3(Fp8Shape<64>::NW * 64), 0, stream, p, v_descale);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<128>), grid, dim3(Fp8Cfg<128>::NW * 64), 0, stream, p, v_descale);
+    hipLaunchKernelGGL((fwd_fp8_kernel<128>), grid, dim3(Fp8Shape<128>::NW * 64), 0, stream, p, v_descale);
   return hipGetLastError();
 }
 
