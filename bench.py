@@ -91,7 +91,7 @@ def per_launch_ms(fn, launches):
         b.record()
     torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in evs)
-    return t[len(t) // 2], sum(t) / len(t)
+    return t[len(t) // 2], sum(t) / len(t), t[0]
 
 
 def load_traffic():
@@ -189,6 +189,55 @@ def stats_summary(stats_dir, workload, cmd):
                     f"median {tail[len(tail) // 2] / 1e3:.2f}  (launches {len(d)})\n")
 
 
+# Counter passes for --pmc-summary: each fits the per-block limits of one
+# rocprofv3 --pmc run (at most 8 SQ and 2 GRBM counters).
+PMC_PASSES = [
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_WAIT_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+    "SQ_INSTS_SALU SQ_ACTIVE_INST_MISC GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_SCA SQ_INST_LEVEL_LDS SQ_LEVEL_WAVES "
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SMEM SQ_INSTS_BRANCH SQ_WAVES",
+]
+PMC_CMD = ("rocprofv3 --pmc {counters} --output-format csv -- python bench.py --workload "
+           "{workload} --steps 5 --warmup 1 --no-cpu-baseline")
+
+
+def pmc_summary(dirs, workload):
+    """Per-kernel counter means (one dispatch) from one rocprofv3 --pmc output
+    directory per pass of PMC_PASSES -> profiles/pmc_<workload>.txt."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if "fa::" not in r["Kernel_Name"]:
+                    continue
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    with open(os.path.join(ROOT, "profiles", f"pmc_{workload}.txt"), "w") as f:
+        f.write(f"rocprofv3 counter summary of bench.py on {workload}: per kernel, the mean of "
+                "each counter over its dispatches (one dispatch's total).\n")
+        for i, c in enumerate(PMC_PASSES):
+            f.write(f"pass {i + 1}: " + PMC_CMD.format(counters=c, workload=workload) + "\n")
+        for name, cs in vals.items():
+            m = {c: sum(v) / len(v) for c, v in cs.items()}
+            f.write(f"\n{name}\n")
+            for c in sorted(m):
+                f.write(f"  {c:28s} {m[c]:.4g}\n")
+            try:
+                f.write(f"  -> per wave-cycle: VALU issuing {m['SQ_ACTIVE_INST_VALU'] / m['SQ_WAVE_CYCLES']:.3f}, "
+                        f"LDS issuing {m['SQ_ACTIVE_INST_LDS'] / m['SQ_WAVE_CYCLES']:.3f}, "
+                        f"waiting {m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f}\n")
+                f.write(f"  -> per MFMA: {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} VALU, "
+                        f"{m['SQ_INSTS_VALU_TRANS_F32'] / m['SQ_INSTS_MFMA']:.2f} transcendental, "
+                        f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} LDS instructions; "
+                        f"LDS bank conflicts {m['SQ_LDS_BANK_CONFLICT']:.0f}\n")
+            except (KeyError, ZeroDivisionError):
+                pass
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle on (batch, head) slices of the same inputs until about
     `seconds` of CPU time have passed; returns TFLOP/s over the slices done."""
@@ -283,6 +332,9 @@ def main():
                     help="after timing, run a plain device copy of this many MiB")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
                     help="write the profiles/ summaries from rocprofv3 output directories")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="ARG",
+                    help="WORKLOAD DIR1 DIR2 DIR3: write profiles/pmc_WORKLOAD.txt from the "
+                         "rocprofv3 --pmc output directories of the three counter passes")
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_DIR", "WORKLOAD"),
                     help="write profiles/kernel_stats_WORKLOAD.txt from a --stats run of "
                          "bench.py --workload WORKLOAD")
@@ -293,6 +345,9 @@ def main():
                   cmds={"fetch": pmc.format(opts="--pmc FETCH_SIZE --output-format csv"),
                         "write": pmc.format(opts="--pmc WRITE_SIZE --output-format csv"),
                         "stats": STATS_CMD.format(workload=METRIC_WORKLOAD_NAME)})
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[1:], args.pmc_summary[0])
         return
     if args.stats_summary:
         stats_summary(args.stats_summary[0], args.stats_summary[1],
@@ -316,7 +371,7 @@ def main():
 
     # The backward is built for bf16 only.
     ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup, backward=w.dtype == "bf16")
-    med_ms, mean_ms = per_launch_ms(fwd, min(args.steps, 100))
+    med_ms, mean_ms, min_ms = per_launch_ms(fwd, min(args.steps, 100))
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -348,6 +403,7 @@ def main():
                      "kernel": {"bf16": "fwd_bf16_kernel", "f32": "fwd_f32_kernel",
                                 "fp8": "fwd_fp8_kernel"}[w.dtype],
                      "launch_ms_mean": round(mean_ms, 5), "launch_ms_median": round(med_ms, 5),
+                     "launch_ms_min": round(min_ms, 5),
                      "algorithmic_bytes": algorithmic_bytes(w)},
         "cpu_baseline": None,
         # The same shape's backward (prep, dK/dV and dQ kernels), counted as

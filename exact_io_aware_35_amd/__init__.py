@@ -9,3 +9,4 @@ from .binding import (  # noqa: F401
     forward_fp8, forward_qkvpacked, load_library, prepare_forward, prepare_forward_fp8,
     workspace_size,
 )
+from .autograd import FlashAttention, flash_attention  # noqa: F401

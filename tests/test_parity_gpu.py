@@ -451,3 +451,27 @@ def test_qkvpacked_alibi_against_oracle():
     ref = attention_backward(*args, np64(d["dout"]), causal=True, alibi_slopes=sl.numpy())
     for i, name in enumerate(("dQ", "dK", "dV")):
         assert_close(dqkv[:, :, i].cpu(), ref[i], TOL["bf16"]["grad"], name, rel=BF16_HALF_ULP)
+
+
+def test_autograd_function_matches_direct_calls_and_oracle():
+    """The torch.autograd wrapper returns the C-ABI forward's O and, through
+    loss.backward(), exactly the gradients a direct fa_backward call gives for
+    dO = d loss / d O; those match the oracle's."""
+    from exact_io_aware_35_amd import flash_attention
+    d = make_case(2, 260, 3, 64, dtype="bf16", seed=31, backward=True, seqlens_k=[260, 190])
+    q, k, v = (dev(d[x]).requires_grad_() for x in ("q", "k", "v"))
+    sk = dev(d["seqlens_k"])
+    out = flash_attention(q, k, v, causal=True, seqlens_k=sk)
+    do = dev(d["dout"])
+    (out.float() * do.float()).sum().backward()
+    torch.cuda.synchronize()
+    o2, lse2 = forward(dev(d["q"]), dev(d["k"]), dev(d["v"]), causal=True, seqlens_k=sk)
+    g2 = backward(dev(d["q"]), dev(d["k"]), dev(d["v"]), o2, lse2, do, causal=True, seqlens_k=sk)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o2)
+    for got, want in zip((q.grad, k.grad, v.grad), g2):
+        assert torch.equal(got, want)
+    rg = attention_backward(np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["dout"]),
+                            causal=True, seqlens_k=d["seqlens_k"].numpy())
+    for name, got, want in zip(("dQ", "dK", "dV"), (q.grad, k.grad, v.grad), rg):
+        assert_close(got.cpu(), want, TOL["bf16"]["grad"], name)
