@@ -71,6 +71,9 @@ WORKLOADS = {
     "fwd_fp8_b2h8n4096d128": Workload(
         "fwd_fp8_b2h8n4096d128", "fp8", 2, 8, 4096, 128, sample_rows=256,
         extra_rows=(0, 1, 4095)),
+    "fwd_fp8_b1h16n65536d128_causal": Workload(
+        "fwd_fp8_b1h16n65536d128_causal", "fp8", 1, 16, 65536, 128,
+        causal=True, sample_rows=256, extra_rows=(0, 1, 4095, 4096, 4097, 65535)),
 }
 
 METRIC_WORKLOAD = "fwd_bf16_b2h8n4096d128"

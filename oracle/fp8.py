@@ -55,15 +55,23 @@ from .attention import _key_len, _softmax_rows, visible_mask, attention_forward,
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(codes):
-    """float64 values of e4m3 codes (uint8 array-like), by the format's definition."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_values(c):
+    """float64 value of each code in the int64 array c, by the format's definition."""
     sign = np.where(c >> 7, -1.0, 1.0)
     e = (c >> 3) & 15
     m = (c & 7).astype(np.float64)
     mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     val = sign * mag
     return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+_E4M3_TABLE = _e4m3_values(np.arange(256, dtype=np.int64))
+
+
+def e4m3_decode(codes):
+    """float64 values of e4m3 codes (uint8 array-like): the definition above,
+    evaluated once per code and looked up (large inputs decode quickly)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_round(x):

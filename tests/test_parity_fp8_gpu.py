@@ -149,16 +149,20 @@ def test_fp8_peaked_rows_follow_one_key():
     assert worst <= 1.0
 
 
-def test_fp8_b2h8n4096d128_sampled_rows():
-    """The full-size shape, launched as the benchmark launches it; 259 query
-    rows per head checked against the oracle."""
-    w = WORKLOADS["fwd_fp8_b2h8n4096d128"]
+@pytest.mark.parametrize("name", ["fwd_fp8_b2h8n4096d128", "fwd_fp8_b1h16n65536d128_causal"])
+def test_fp8_workload_sampled_rows(name):
+    """The full-size shapes, launched as the benchmark launches them: the
+    metric shape and the 64K causal shape, 259 or 262 query rows per head
+    (the causal one includes the first, last and 4096-boundary rows) checked
+    against the oracle."""
+    w = WORKLOADS[name]
     d = make_inputs(w, 0)
     o, lse = run(d, w.causal, w.window)
     rows = d["rows"].numpy()
     args = oracle_args(d)
-    ro, rl = attention_forward_fp8_rows(*args, rows=rows, softmax_scale=w.softmax_scale)
-    bnd = fp8_output_bound(*args, softmax_scale=w.softmax_scale, rows=rows)
+    mask = dict(softmax_scale=w.softmax_scale, causal=w.causal, window=w.window)
+    ro, rl = attention_forward_fp8_rows(*args, rows=rows, **mask)
+    bnd = fp8_output_bound(*args, rows=rows, **mask)
     got_o = np.stack([o[:, rows[h], h, :] for h in range(w.heads)], axis=1)
     got_l = np.stack([lse[:, h, rows[h]] for h in range(w.heads)], axis=1)
     assert_fp8_close(got_o, ro, bnd, w.seqlen)
