@@ -176,8 +176,9 @@ def forward_fp8(q8, k8, v8, descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=
     if k8.shape != q8.shape or v8.shape != q8.shape:
         raise FaError(FA_ERR_INVALID_ARG, "q8, k8, v8 must have the same shape")
     for t, name in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
-        if t.element_size() != 1:
-            raise FaError(FA_ERR_INVALID_ARG, f"{name} must hold one byte per element")
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise FaError(FA_ERR_INVALID_ARG,
+                          f"{name} must be torch.uint8 (e4m3 bytes) or torch.float8_e4m3fn")
     lib = load_library()
     B, N, H, D = q8.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -232,6 +233,11 @@ def prepare_forward(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_sc
 def prepare_forward_fp8(q8, k8, v8, out, lse, descale_q, descale_k, descale_v, causal=False,
                         window=(-1, -1), softmax_scale=None, seqlens_k=None, stream=None):
     """forward_fp8() with every argument marshalled once; returns a callable."""
+    import torch
+    for t, name in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise FaError(FA_ERR_INVALID_ARG,
+                          f"{name} must be torch.uint8 (e4m3 bytes) or torch.float8_e4m3fn")
     lib = load_library()
     B, N, H, D = q8.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)

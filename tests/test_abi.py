@@ -216,3 +216,10 @@ def test_fp8_slice_limit_counts_one_byte_per_element():
     # past the size check and stops at the null lse.
     assert fwd_fp8(lib, H=64, N=1 << 17, D=128, lse=None) == fb.FA_ERR_INVALID_ARG
     assert "lse is null" in lib.fa_last_error_message().decode()
+
+
+def test_fp8_binding_rejects_other_byte_types():
+    import torch
+    x = torch.zeros((1, 4, 1, 64), dtype=torch.float8_e5m2)
+    with pytest.raises(fb.FaError, match="e4m3"):
+        fb.forward_fp8(x, x, x)
