@@ -135,3 +135,34 @@ def make_case(batch, seqlen, heads, headdim, dtype="bf16", std=1.0, seed=0,
     if seqlens_k is not None:
         d["seqlens_k"] = torch.as_tensor(seqlens_k, dtype=torch.int32)
     return d
+
+
+# Hashed inputs for sizes too large to draw on the host. Element (i, h, d) of
+# tensor `kind` is (table index - 128) / 64 with the index
+# (a_kind(i) + b_kind(h, d)) mod 256, a and b integer hashes. Every value is a
+# multiple of 1/64 in [-2, 2), exact in bf16, and any subset of rows can be
+# rebuilt on the CPU without the rest.
+_HASH_MUL = {"q": 2654435761, "k": 2246822519, "v": 3266489917, "dout": 668265263}
+
+
+def hashed_rows(kind, rows, heads, headdim, device="cpu"):
+    """bf16 [len(rows), heads, headdim] of hashed tensor `kind` at sequence
+    positions `rows` (an int64 tensor)."""
+    mul = _HASH_MUL[kind]
+    rows = torch.as_tensor(rows, dtype=torch.int64, device=device)
+    a = ((rows * mul) >> 11) & 255                                  # [R]
+    hd = torch.arange(heads * headdim, dtype=torch.int64, device=device)
+    b = ((hd * (mul | 1) + 12345) >> 7) & 255                       # [H*D]
+    idx = (a[:, None] + b[None, :]) & 255
+    val = ((idx - 128).to(torch.float32) / 64.0).to(torch.bfloat16)
+    return val.view(len(rows), heads, headdim)
+
+
+def hashed_tensor(kind, batch, seqlen, heads, headdim, device, chunk=1 << 20):
+    """The whole [batch, seqlen, heads, headdim] hashed tensor (all batch
+    entries alike), built on `device` in chunks of rows."""
+    out = torch.empty((batch, seqlen, heads, headdim), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, seqlen, chunk):
+        r1 = min(seqlen, r0 + chunk)
+        out[:, r0:r1] = hashed_rows(kind, torch.arange(r0, r1), heads, headdim, device)
+    return out
