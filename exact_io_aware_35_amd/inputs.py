@@ -166,3 +166,26 @@ def hashed_tensor(kind, batch, seqlen, heads, headdim, device, chunk=1 << 20):
         r1 = min(seqlen, r0 + chunk)
         out[:, r0:r1] = hashed_rows(kind, torch.arange(r0, r1), heads, headdim, device)
     return out
+
+
+def hashed_fp8_rows(kind, rows, heads, headdim, device="cpu"):
+    """e4m3 bytes (torch.uint8) [len(rows), heads, headdim] of hashed tensor
+    `kind`: sign, exponent field 5..8 and mantissa taken from the hash, so
+    every byte is a finite value of magnitude 0.25 .. 3.75 (no NaN code)."""
+    mul = _HASH_MUL[kind]
+    rows = torch.as_tensor(rows, dtype=torch.int64, device=device)
+    a = ((rows * mul) >> 11) & 255
+    hd = torch.arange(heads * headdim, dtype=torch.int64, device=device)
+    b = ((hd * (mul | 1) + 12345) >> 7) & 255
+    idx = (a[:, None] + b[None, :]) & 255
+    code = ((idx >> 7) << 7) | ((5 + ((idx >> 3) & 3)) << 3) | (idx & 7)
+    return code.to(torch.uint8).view(len(rows), heads, headdim)
+
+
+def hashed_fp8_tensor(kind, batch, seqlen, heads, headdim, device, chunk=1 << 20):
+    """The whole [batch, seqlen, heads, headdim] hashed e4m3 tensor on `device`."""
+    out = torch.empty((batch, seqlen, heads, headdim), dtype=torch.uint8, device=device)
+    for r0 in range(0, seqlen, chunk):
+        r1 = min(seqlen, r0 + chunk)
+        out[:, r0:r1] = hashed_fp8_rows(kind, torch.arange(r0, r1), heads, headdim, device)
+    return out

@@ -68,3 +68,43 @@ def test_max_size_slice(run, c):
     print(c, {"O": err_o, "LSE": err_l, "dQ": err_dq, "dK": err_dk, "dV": err_dv}, flush=True)
     assert err_o <= 2e-2 and err_l <= 1e-3
     assert err_dq <= 2e-2 and err_dk <= 2e-2 and err_dv <= 2e-2
+
+
+# fp8: one byte per element, so the largest slice is twice as long:
+# (16777087 + 128) * 128 bytes < 2^31 <= (16777088 + 128) * 128.
+N8 = 16777087
+DESC = (0.25, 0.25, 0.5)
+
+
+@pytest.fixture(scope="module")
+def run_fp8():
+    from exact_io_aware_35_amd import forward_fp8
+    from exact_io_aware_35_amd.inputs import hashed_fp8_tensor
+    print(f"max-size fp8 case: B1 H{H} N{N8} D{D} window {WIN} causal", flush=True)
+    q, k, v = (hashed_fp8_tensor(n, 1, N8, H, D, DEV) for n in ("q", "k", "v"))
+    o, lse = forward_fp8(q, k, v, *DESC, causal=True, window=WIN)
+    torch.cuda.synchronize()
+    del q, k, v
+    yield o, lse
+    del o, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("c", [0, 65536 + 31, N8 // 2, N8 - 1])
+def test_max_size_fp8_slice(run_fp8, c):
+    from exact_io_aware_35_amd.inputs import hashed_fp8_rows
+    from oracle.fp8 import attention_forward_fp8, fp8_output_bound
+    o, lse = run_fp8
+    a, b = max(0, c - 128), min(N8, c + 129)
+    rows = torch.arange(a, b)
+    q8, k8, v8 = (hashed_fp8_rows(n, rows, H, D).numpy()[None] for n in ("q", "k", "v"))
+    ro, rl = attention_forward_fp8(q8, k8, v8, *DESC, causal=True, window=WIN)
+    bnd = fp8_output_bound(q8, k8, v8, *DESC, causal=True, window=WIN)
+    lo = a if a == 0 else a + 64
+    f = slice(lo - a, b - a)
+    got = o[0, lo:b].float().cpu().numpy().astype(np.float64)
+    tol = bnd[0, f] * (1 + 2.0 ** -8 + 16 * (65 * 2.0 ** -24 + 1e-3)) + 2.0 ** -8 * np.abs(ro[0, f]) + 1e-6
+    err = np.abs(got - ro[0, f])
+    err_l = np.abs(lse[0, 0, lo:b].cpu().numpy() - rl[0, 0, f]).max()
+    print(c, {"O worst/bound": float((err / tol).max()), "LSE": err_l}, flush=True)
+    assert (err <= tol).all() and err_l <= 1e-3
