@@ -33,7 +33,7 @@ METRIC_WORKLOAD_NAME = "fwd_bf16_b2h8n4096d128"
 STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -- python bench.py "
              "--workload {workload} --steps 200 --warmup 50 --no-cpu-baseline")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "fp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_b2h8n4096d128.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_35_amd", "csrc", f)
@@ -59,7 +59,7 @@ def algorithmic_bytes(w):
     n = w.batch * w.seqlen * w.heads * w.headdim
     if w.dtype == "fp8":  # e4m3 inputs, bf16 output
         return 3 * n + 2 * n + w.batch * w.heads * w.seqlen * 4
-    esz = 2 if w.dtype == "bf16" else 4
+    esz = 4 if w.dtype == "f32" else 2
     return 4 * n * esz + w.batch * w.heads * w.seqlen * 4
 
 
@@ -138,8 +138,8 @@ def summarize(fetch_dir, write_dir, stats_dir, copy_mib, cmds):
     wcsv = glob.glob(os.path.join(write_dir, "**", "*counter_collection.csv"), recursive=True)[0]
     fetch = _counter_means(fcsv, "FETCH_SIZE")
     write = _counter_means(wcsv, "WRITE_SIZE")
-    attn = [k for k in fetch if "fwd_bf16_kernel" in k][0]
-    copy = [k for k in fetch if "fwd_bf16_kernel" not in k and "opy" in k or "elementwise" in k]
+    attn = [k for k in fetch if "fwd_h16_kernel" in k][0]
+    copy = [k for k in fetch if "fwd_h16_kernel" not in k and "opy" in k or "elementwise" in k]
     copy = max(copy, key=lambda k: fetch[k])
     known = copy_mib * (1 << 20)
     f_scale = known / (fetch[copy] * 1024.0)
@@ -369,8 +369,9 @@ def main():
     print(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}",
           file=sys.stderr, flush=True)
 
-    # The backward is built for bf16 only.
-    ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup, backward=w.dtype == "bf16")
+    # The backward is built for the 16-bit types.
+    ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup,
+                                        backward=w.dtype in ("bf16", "f16"))
     med_ms, mean_ms, min_ms = per_launch_ms(fwd, min(args.steps, 100))
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -400,8 +401,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": traffic if w.name == METRIC_WORKLOAD_NAME else None,
-                     "kernel": {"bf16": "fwd_bf16_kernel", "f32": "fwd_f32_kernel",
-                                "fp8": "fwd_fp8_kernel"}[w.dtype],
+                     "kernel": {"bf16": "fwd_h16_kernel<bf16>", "f16": "fwd_h16_kernel<fp16>",
+                                "f32": "fwd_f32_kernel", "fp8": "fwd_fp8_kernel"}[w.dtype],
                      "launch_ms_mean": round(mean_ms, 5), "launch_ms_median": round(med_ms, 5),
                      "launch_ms_min": round(min_ms, 5),
                      "algorithmic_bytes": algorithmic_bytes(w)},

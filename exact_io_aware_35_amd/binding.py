@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F32 = 1
+FA_DTYPE_F16 = 2
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = 1
@@ -83,6 +84,8 @@ def _dtype_code(t):
         return FA_DTYPE_BF16
     if t.dtype == torch.float32:
         return FA_DTYPE_F32
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
     raise FaError(FA_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported")
 
 

@@ -15,6 +15,11 @@ namespace {
 
 thread_local char g_msg[256] = "";
 
+fa::ElemType elem_type(fa_dtype_t dtype) {
+  return dtype == FA_DTYPE_F32 ? fa::ElemType::kF32
+       : dtype == FA_DTYPE_F16 ? fa::ElemType::kF16 : fa::ElemType::kBF16;
+}
+
 fa_status_t fail(fa_status_t s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -36,7 +41,7 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
     return fail(FA_ERR_INVALID_ARG, "seqlen %d exceeds 2^24", seqlen);
   if ((long long)batch * heads * seqlen >= (1LL << 31))
     return fail(FA_ERR_INVALID_ARG, "batch*heads*seqlen must be < 2^31");
-  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32)
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_UNSUPPORTED, "dtype %d is not supported", (int)dtype);
   if (headdim != 64 && headdim != 128)
     return fail(FA_ERR_UNSUPPORTED, "headdim %d is not supported (64 or 128)", headdim);
@@ -168,7 +173,7 @@ fa_status_t fa_forward_ex(const void* q, const void* k, const void* v, int qkv_p
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
   if ((s = check_alibi(alibi_slopes, alibi_batch_stride, heads)) != FA_OK) return s;
 
-  const int f32 = dtype == FA_DTYPE_F32;
+  const fa::ElemType et = elem_type(dtype);
   fa::FwdParams p{};
   p.q = qkv[0]; p.k = qkv[1]; p.v = qkv[2]; p.o = out; p.lse = lse;
   p.mask.seqlens_k = seqlens_k;
@@ -179,14 +184,14 @@ fa_status_t fa_forward_ex(const void* q, const void* k, const void* v, int qkv_p
   p.B = batch; p.H = heads; p.N = seqlen;
   p.rs_q = rs_q;
   p.rs_o = heads * headdim;
-  const int bm = fa::fwd_block_rows(f32, headdim);
+  const int bm = fa::fwd_block_rows(et, headdim);
   p.nqb = (seqlen + bm - 1) / bm;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.xcd_groups = (batch * heads) % 8 == 0 ? 1 : 0;
   p.longest_first = wr >= 0 ? 1 : 0;
   if ((long long)batch * heads * p.nqb >= (1LL << 31))
     return fail(FA_ERR_INVALID_ARG, "grid too large");
-  hipError_t e = fa::launch_forward(p, headdim, f32, stream);
+  hipError_t e = fa::launch_forward(p, headdim, et, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -269,8 +274,8 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
   fa_status_t s = check_common(batch, heads, seqlen, headdim, softmax_scale, causal,
                                window_left, window_right, dtype, &wl, &wr, qkv_packed ? 3 : 1);
   if (s != FA_OK) return s;
-  if (dtype != FA_DTYPE_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+    return fail(FA_ERR_UNSUPPORTED, "the backward is built for bf16 and fp16 only");
   void* qkv[3];
   int rs_q;
   if ((s = resolve_qkv(q, k, v, qkv_packed, heads, headdim, dtype, kQkvNames, qkv, &rs_q)) !=
@@ -318,7 +323,7 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
   p.scale = softmax_scale;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.xcd_groups = (batch * heads) % 8 == 0 ? 1 : 0;
-  hipError_t e = fa::launch_backward(p, headdim, dtype == FA_DTYPE_F32, stream);
+  hipError_t e = fa::launch_backward(p, headdim, elem_type(dtype), stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return FA_OK;
 }

@@ -42,8 +42,9 @@ namespace fa {
 // One 16-byte chunk of one (b, i, h) row per thread: D_i = sum_d dO O (fp32),
 // the fp16 copies of the Q, K and dO chunks, and per row the statistics pair
 // (LSE log2 e, or +inf for a row with no visible key; D_i).
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
+  using E = Elt16<T>;
   constexpr int LPR = D / 8;               // lanes per row, 16 bytes each
   constexpr int RPB = 256 / LPR;           // rows per block
   const int tid = threadIdx.x;
@@ -56,16 +57,16 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
     const size_t hd = (size_t)(r - bi * p.H) * D + 8 * c;
     const size_t e = (size_t)r * D + 8 * c;       // the fp16 copies are [B][N][H][D]
     const size_t eq = (size_t)bi * p.rs_q + hd, eo = (size_t)bi * p.rs_o + hd;
-    const u32x4_t o = ld_global<u32x4_t>((const __bf16*)p.o + eo);
-    const u32x4_t g = ld_global<u32x4_t>((const __bf16*)p.dout + eo);
-    const u32x4_t q = ld_global<u32x4_t>((const __bf16*)p.q + eq);
-    const u32x4_t k = ld_global<u32x4_t>((const __bf16*)p.k + eq);
+    const u32x4_t o = ld_global<u32x4_t>((const T*)p.o + eo);
+    const u32x4_t g = ld_global<u32x4_t>((const T*)p.dout + eo);
+    const u32x4_t q = ld_global<u32x4_t>((const T*)p.q + eq);
+    const u32x4_t k = ld_global<u32x4_t>((const T*)p.k + eq);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc += bf16_lo(o[j]) * bf16_lo(g[j]) + bf16_hi(o[j]) * bf16_hi(g[j]);
-    *(u32x4_t*)((_Float16*)p.do16 + e) = bf16x8_to_f16x8(g);
-    *(u32x4_t*)((_Float16*)p.q16 + e) = bf16x8_to_f16x8(q);
-    *(u32x4_t*)((_Float16*)p.k16 + e) = bf16x8_to_f16x8(k);
+      acc += E::lo(o[j]) * E::lo(g[j]) + E::hi(o[j]) * E::hi(g[j]);
+    *(u32x4_t*)((_Float16*)p.do16 + e) = E::to_f16x8(g);
+    *(u32x4_t*)((_Float16*)p.q16 + e) = E::to_f16x8(q);
+    *(u32x4_t*)((_Float16*)p.k16 + e) = E::to_f16x8(k);
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -105,8 +106,9 @@ struct KvCfg {
 //                                    packed to fp16 straight from the accumulators).
 // Query rows at or past N arrive as zeros (Q, dO and both statistics), which
 // makes every term they add zero.
-template <int D, bool ALIBI>
+template <int D, bool ALIBI, typename T>
 __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p) {
+  using E = Elt16<T>;
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF];
 
@@ -137,7 +139,7 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       kf[s] = ld_global<f16x8_t>((const _Float16*)p.k16 + off + 16 * s);
-      vf[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + voff + 16 * s)));
+      vf[s] = __builtin_bit_cast(f16x8_t, E::to_f16x8(ld_global<u32x4_t>((const T*)p.v + voff + 16 * s)));
     }
   }
 
@@ -326,18 +328,18 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 
   }
   if (key < N) {
-    __bf16* dkrow = (__bf16*)p.dk + gbase + (size_t)key * p.rs_g;
-    __bf16* dvrow = (__bf16*)p.dv + gbase + (size_t)key * p.rs_g;
+    T* dkrow = (T*)p.dk + gbase + (size_t)key * p.rs_g;
+    T* dvrow = (T*)p.dv + gbase + (size_t)key * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
         *(u32x2_t*)(dkrow + col) =
-            u32x2_t{pack_bf16x2(dk[d][4 * g] * p.scale, dk[d][4 * g + 1] * p.scale),
-                    pack_bf16x2(dk[d][4 * g + 2] * p.scale, dk[d][4 * g + 3] * p.scale)};
-        *(u32x2_t*)(dvrow + col) = u32x2_t{pack_bf16x2(dv[d][4 * g], dv[d][4 * g + 1]),
-                                           pack_bf16x2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
+            u32x2_t{E::pack2(dk[d][4 * g] * p.scale, dk[d][4 * g + 1] * p.scale),
+                    E::pack2(dk[d][4 * g + 2] * p.scale, dk[d][4 * g + 3] * p.scale)};
+        *(u32x2_t*)(dvrow + col) = u32x2_t{E::pack2(dv[d][4 * g], dv[d][4 * g + 1]),
+                                           E::pack2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
       }
   }
 }
@@ -370,8 +372,9 @@ struct KvPairCfg {
 // A work-group barrier between the two phases of a tile hands P over; the
 // MFMA work is the same as in the one-wave form. P crosses in fp16, the
 // precision of its own MFMA operand, so dS is formed from the P that dV uses.
-template <int D, bool ALIBI>
+template <int D, bool ALIBI, typename T>
 __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(BwdParams p) {
+  using E = Elt16<T>;
   using C = KvPairCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF + C::NP * C::XCH];
 
@@ -406,7 +409,7 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
       const size_t off = vbase + (size_t)kr * p.rs_q + 8 * hf;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s)
-        kv[s] = __builtin_bit_cast(f16x8_t, bf16x8_to_f16x8(ld_global<u32x4_t>((const __bf16*)p.v + off + 16 * s)));
+        kv[s] = __builtin_bit_cast(f16x8_t, E::to_f16x8(ld_global<u32x4_t>((const T*)p.v + off + 16 * s)));
     }
   }
 
@@ -628,15 +631,15 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
   // of its key.
   if (key < N) {
     const float sc = role == 0 ? 1.f : p.scale;
-    __bf16* row = (__bf16*)(role == 0 ? p.dv : p.dk) + gbase + (size_t)key * p.rs_g;
+    T* row = (T*)(role == 0 ? p.dv : p.dk) + gbase + (size_t)key * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
         *(u32x2_t*)(row + col) =
-            u32x2_t{pack_bf16x2(acc[d][4 * g] * sc, acc[d][4 * g + 1] * sc),
-                    pack_bf16x2(acc[d][4 * g + 2] * sc, acc[d][4 * g + 3] * sc)};
+            u32x2_t{E::pack2(acc[d][4 * g] * sc, acc[d][4 * g + 1] * sc),
+                    E::pack2(acc[d][4 * g + 2] * sc, acc[d][4 * g + 3] * sc)};
       }
   }
 }
@@ -663,8 +666,10 @@ struct DqCfg {
 //   dQ^T += K^T dS^T                    (A: transposed K reads; B: dS^T packed
 //                                       to fp16 from the accumulators).
 // K comes from the fp16 copy (its products meet dS), V stays bf16.
-template <int D, bool ALIBI>
+template <int D, bool ALIBI, typename T>
 __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) {
+  using E = Elt16<T>;
+  using vec8 = typename E::vec8;
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];  // [buf][K | V]
 
@@ -695,14 +700,14 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   // This lane's query row: Q (fp16) and dO (bf16) as B operands, LSE2 and D.
   const int qi = wq0 + ln, qrow = min(qi, N - 1);
   f16x8_t qf[C::DS];
-  bf16x8_t of[C::DS];
+  vec8 of[C::DS];
   {
     const size_t off = base + (size_t)qrow * rs + 8 * hf;
     const size_t ooff = obase + (size_t)qrow * p.rs_o + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       qf[s] = ld_global<f16x8_t>((const _Float16*)p.q16 + off + 16 * s);
-      of[s] = ld_global<bf16x8_t>((const __bf16*)p.dout + ooff + 16 * s);
+      of[s] = ld_global<vec8>((const T*)p.dout + ooff + 16 * s);
     }
   }
   const f32x2_t st = ld_global<f32x2_t>(p.stats + 2 * (((size_t)b * p.H + h) * N + qrow));
@@ -713,7 +718,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   const __amdgpu_buffer_rsrc_t krsrc =
       make_rsrc((const _Float16*)p.k16 + base, ((N - 1) * rs + D) * 2);
   const __amdgpu_buffer_rsrc_t vrsrc =
-      make_rsrc((const __bf16*)p.v + vbase, ((N - 1) * p.rs_q + D) * 2);
+      make_rsrc((const T*)p.v + vbase, ((N - 1) * p.rs_q + D) * 2);
   int kloff[C::LPW], vloff[C::LPW];
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
@@ -760,7 +765,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
       for (int s = 0; s < C::DS; ++s) {
         const int off = kb * 32 * C::CPR * 16 + roff[s];
         sa = mfma_f16(*(const f16x8_t*)(sk + off), qf[s], sa);
-        pa = mfma_bf16(*(const bf16x8_t*)(sv + off), of[s], pa);
+        pa = E::mfma(*(const vec8*)(sv + off), of[s], pa);
       }
       if constexpr (ALIBI) {  // row i, key j: q.k - (slope / c) |i - j|
         const float di = (float)(qi - kt - 32 * kb - 4 * hf);
@@ -814,51 +819,57 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   }
 
   if (qi < N) {
-    __bf16* row = (__bf16*)p.dq + gbase + (size_t)qi * p.rs_g;
+    T* row = (T*)p.dq + gbase + (size_t)qi * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
         *(u32x2_t*)(row + col) =
-            u32x2_t{pack_bf16x2(dq[d][4 * g] * p.scale, dq[d][4 * g + 1] * p.scale),
-                    pack_bf16x2(dq[d][4 * g + 2] * p.scale, dq[d][4 * g + 3] * p.scale)};
+            u32x2_t{E::pack2(dq[d][4 * g] * p.scale, dq[d][4 * g + 1] * p.scale),
+                    E::pack2(dq[d][4 * g + 2] * p.scale, dq[d][4 * g + 3] * p.scale)};
       }
   }
 }
 
 // ---------------------------------------------------------------- launcher
 
-template <int D, bool ALIBI>
+template <int D, bool ALIBI, typename T>
 static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.N * p.H;
   const long long rpb = 256 / (D / 8);
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_prep_kernel<D, T>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
                      stream, p);
   // Measured on MI355X: the one-wave form is faster at headdim 64 (two
   // waves per SIMD either way, half the barriers); at headdim 128 only the
   // pair form keeps its state in VGPRs.
   if constexpr (D == 128) {
     p.nblk = (p.N + KvPairCfg<D>::BK - 1) / KvPairCfg<D>::BK;
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, ALIBI>), dim3(p.B * p.H * p.nblk),
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, ALIBI, T>), dim3(p.B * p.H * p.nblk),
                        dim3(KvPairCfg<D>::NW * 64), 0, stream, p);
   } else {
     p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(p.B * p.H * p.nblk),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI, T>), dim3(p.B * p.H * p.nblk),
                        dim3(KvCfg<D>::NW * 64), 0, stream, p);
   }
   p.nblk = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI, T>), dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64),
                      0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_backward(BwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
-  if (dtype_is_f32) return hipErrorNotSupported;
+template <typename T>
+static hipError_t launch_backward_t(BwdParams p, int headdim, hipStream_t stream) {
   const bool alibi = p.alibi.slopes != nullptr;
   if (headdim == 64)
-    return alibi ? launch_backward_d<64, true>(p, stream) : launch_backward_d<64, false>(p, stream);
-  return alibi ? launch_backward_d<128, true>(p, stream) : launch_backward_d<128, false>(p, stream);
+    return alibi ? launch_backward_d<64, true, T>(p, stream) : launch_backward_d<64, false, T>(p, stream);
+  return alibi ? launch_backward_d<128, true, T>(p, stream) : launch_backward_d<128, false, T>(p, stream);
+}
+
+hipError_t launch_backward(BwdParams p, int headdim, ElemType et, hipStream_t stream) {
+  if (et == ElemType::kF32) return hipErrorNotSupported;
+  if (et == ElemType::kF16) return launch_backward_t<_Float16>(p, headdim, stream);
+  return launch_backward_t<__bf16>(p, headdim, stream);
 }
 
 }  // namespace fa

@@ -163,6 +163,37 @@ __device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t u) {
   return r;
 }
 
+// The two 16-bit element types of Q, K, V, O, dO and the gradients: bf16 and
+// fp16 (IEEE half). Both run on the 32x32x16 MFMA with fp32 accumulation and
+// round their outputs to nearest even.
+template <typename T>
+struct Elt16;
+template <>
+struct Elt16<__bf16> {
+  using vec8 = bf16x8_t;
+  static constexpr bool is_f16 = false;
+  static __device__ __forceinline__ f32x16_t mfma(vec8 a, vec8 b, f32x16_t c) { return mfma_bf16(a, b, c); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ float lo(uint32_t u) { return bf16_lo(u); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return bf16_hi(u); }
+  // 8 values -> 8 fp16 values (the backward's operand format).
+  static __device__ __forceinline__ u32x4_t to_f16x8(u32x4_t u) { return bf16x8_to_f16x8(u); }
+};
+template <>
+struct Elt16<_Float16> {
+  using vec8 = f16x8_t;
+  static constexpr bool is_f16 = true;
+  static __device__ __forceinline__ f32x16_t mfma(vec8 a, vec8 b, f32x16_t c) { return mfma_f16(a, b, c); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_f16x2(a, b); }
+  static __device__ __forceinline__ float lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(u & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16));
+  }
+  static __device__ __forceinline__ u32x4_t to_f16x8(u32x4_t u) { return u; }
+};
+
 // LDS tiles of 16-bit values, [rows][D] row-major, with the 16-byte chunks of
 // each row XOR-swizzled: chunk c of row r is stored at position c ^ lds_swz(r).
 // With it the two read patterns of the kernels are free of bank conflicts:

@@ -16,8 +16,9 @@
 // by 2^(M_old - M_new) when M changes. Rescaling is lazy: M is only raised when
 // some row's tile max exceeds it by more than 8 (log2 units), so P values stay
 // <= 2^8; O and l always share the same M, so the result is unchanged up to
-// rounding. O^T += V^T P^T then runs on MFMA with P packed to bf16 straight
-// from the score accumulators, in the key order the accumulator holds them.
+// rounding. O^T += V^T P^T then runs on MFMA with P packed to the input type
+// (bf16 or fp16) straight from the score accumulators, in the key order the
+// accumulator holds them.
 //
 // Epilogue: O = O_acc / l rounded to the output dtype; LSE = (M + log2 l) ln 2
 // (from-scratch article §3.1 LSE statistic, §5.2 fp32 statistics).
@@ -54,21 +55,25 @@ struct FwdCfg {
   static_assert(LPW >= 1 && TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads");
 };
 
-// bf16 forward. One work-group = 4 waves x 64 query rows. K and V tiles are
-// copied global -> LDS by the 16-byte direct-to-LDS loads (no staging
+// 16-bit (bf16 or fp16) forward. One work-group = NW waves x 32 query rows
+// (FwdShape). K and V tiles are copied global -> LDS by the 16-byte
+// direct-to-LDS loads (no staging
 // registers), double-buffered: the copy of tile t+1 is in flight while tile t
 // is computed. Rows past the end of the sequence are clamped onto the last
 // row (their scores are masked to -inf, so their values never contribute).
 //
 // Per tile and wave: S^T = K Q^T on 32x32x16 MFMA (each lane holds the scores
-// of two query rows, ln and 32 + ln, for 16 keys per 32-key block); online
+// of query row ln for 16 keys per 32-key block, the other 16 in the lane of
+// the other 32-lane half); online
 // softmax with a lazily raised reference max; O^T += V^T P^T with the V^T
 // operand read by ds_read_b64_tr_b16 (lane i of a 16-lane group receives
 // element (4e + i/4, i%4) of the 16 x 4 block the group addresses, so each
 // lane points at 4 values of one key row and gets 4 keys of one d column).
-template <int D, bool ALIBI>
-__global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams p) {
+template <int D, bool ALIBI, typename T>
+__global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
+  using E = Elt16<T>;
+  using vec8 = typename E::vec8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::NBUF * C::TILE];  // [buf][K | V]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -82,10 +87,10 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
   const int kl = key_len(p.mask, b, N);
   const int rs = p.rs_q;                                // elements between sequence positions
   const size_t base = (size_t)b * N * rs + (size_t)h * D;  // element (b, 0, h, 0)
-  const __bf16* Q = (const __bf16*)p.q + base;
-  const char* Kg = (const char*)((const __bf16*)p.k + base);
-  const char* Vg = (const char*)((const __bf16*)p.v + base);
-  __bf16* O = (__bf16*)p.o + (size_t)b * N * p.rs_o + (size_t)h * D;
+  const T* Q = (const T*)p.q + base;
+  const char* Kg = (const char*)((const T*)p.k + base);
+  const char* Vg = (const char*)((const T*)p.v + base);
+  T* O = (T*)p.o + (size_t)b * N * p.rs_o + (size_t)h * D;
   float slope_raw = 0.f;
   if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
 
@@ -98,12 +103,12 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
   if (wq0 <= wq1) key_range(p.mask, kl, wq0, wq1, wklo, wkhi);
 
   // Q as the B operand of S^T = K Q^T: qf[qb][s] = Q[wq0 + 32 qb + ln][16 s + 8 hf ..+8).
-  bf16x8_t qf[C::QB][C::DS];
+  vec8 qf[C::QB][C::DS];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const int row = min(wq0 + 32 * qb + ln, N - 1);     // rows past N are computed, never stored
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) qf[qb][s] = ld_global<bf16x8_t>(Q + (size_t)row * rs + 16 * s + 8 * hf);
+    for (int s = 0; s < C::DS; ++s) qf[qb][s] = ld_global<vec8>(Q + (size_t)row * rs + 16 * s + 8 * hf);
   }
 
   // Direct-to-LDS copy through buffer loads: load j of this wave fills LDS
@@ -178,9 +183,9 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     for (int s = 0; s < C::DS; ++s)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8_t kop = *(const bf16x8_t*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
+        const vec8 kop = *(const vec8*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = mfma_bf16(kop, qf[qb][s], sacc[kb][qb]);
+        for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = E::mfma(kop, qf[qb][s], sacc[kb][qb]);
       }
     if constexpr (ALIBI) {  // score of row i, key j: q.k - (slope / c) |i - j|
 #pragma unroll
@@ -223,7 +228,9 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     // The fast path therefore skips the tile max and checks the tile's row
     // sums instead: if any exceeds 2^64 (or M is still -inf for some row),
     // the tile is redone on the exact path, which raises M to the running max
-    // and rescales O and l. P <= 2^64 keeps O and l far inside fp32 range.
+    // and rescales O and l. P <= 2^64 keeps O and l far inside fp32 range;
+    // with fp16 operands the bound is 2^15, so every P fits fp16 (max 65504).
+    constexpr float kPmax = E::is_f16 ? 32768.f : 0x1p64f;
     u32x4_t pk[C::QB][C::KS];
     float rsum[C::QB];
     auto exps = [&](const float (&m_use)[C::QB]) {
@@ -237,7 +244,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
             const float p0 = exp2_fast(fmaf(sacc[kb][qb][i], p.scale_log2, -m_use[qb]));
             const float p1 = exp2_fast(fmaf(sacc[kb][qb][i + 1], p.scale_log2, -m_use[qb]));
             acc += p0 + p1;  // fp32 sum of the unrounded P (LSE must hold to 1e-3 on short rows)
-            pk[qb][2 * kb + (i >> 3)][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+            pk[qb][2 * kb + (i >> 3)][(i & 7) >> 1] = E::pack2(p0, p1);
           }
         rsum[qb] = acc;
       }
@@ -247,7 +254,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
       exps(m_ref);
       bool big = false;
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) big |= !(rsum[qb] <= 0x1p64f);
+      for (int qb = 0; qb < C::QB; ++qb) big |= !(rsum[qb] <= kPmax);
       slow = __builtin_amdgcn_readfirstlane(__ballot(big) != 0);
     }
     if (slow) {  // wave-uniform, rare: first visible tile, or a score far above M
@@ -284,8 +291,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
         const u32x4_t a = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb)
-          oacc[d][qb] = mfma_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, pk[qb][ks]),
-                                  oacc[d][qb]);
+          oacc[d][qb] = E::mfma(__builtin_bit_cast(vec8, a), __builtin_bit_cast(vec8, pk[qb][ks]), oacc[d][qb]);
       }
   };
 
@@ -318,15 +324,15 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_bf16_kernel(FwdParams 
     const float l = half_sum(l_part[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qi < N) {
-      __bf16* orow = O + (size_t)qi * p.rs_o;
+      T* orow = O + (size_t)qi * p.rs_o;
 #pragma unroll
       for (int d = 0; d < C::DB; ++d)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = 32 * d + 8 * g + 4 * hf;
           *(u32x2_t*)(orow + col) =
-              u32x2_t{pack_bf16x2(oacc[d][qb][4 * g] * inv, oacc[d][qb][4 * g + 1] * inv),
-                      pack_bf16x2(oacc[d][qb][4 * g + 2] * inv, oacc[d][qb][4 * g + 3] * inv)};
+              u32x2_t{E::pack2(oacc[d][qb][4 * g] * inv, oacc[d][qb][4 * g + 1] * inv),
+                      E::pack2(oacc[d][qb][4 * g + 2] * inv, oacc[d][qb][4 * g + 3] * inv)};
         }
       if (hf == 0)
         p.lse[((size_t)b * p.H + h) * N + qi] =
@@ -483,28 +489,36 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams p) {
 
 // ---------------------------------------------------------------- launchers
 
-int fwd_block_rows(int dtype_is_f32, int headdim) {
-  if (dtype_is_f32) return 128;
+int fwd_block_rows(ElemType et, int headdim) {
+  if (et == ElemType::kF32) return 128;
   return headdim == 64 ? FwdCfg<64>::BM : FwdCfg<128>::BM;
 }
 
-template <bool ALIBI>
-static void launch_forward_a(const FwdParams& p, int headdim, int dtype_is_f32, hipStream_t stream) {
+template <bool ALIBI, typename T>
+static void launch_forward_h16(const FwdParams& p, int headdim, hipStream_t stream) {
   const dim3 grid(p.B * p.H * p.nqb);
-  if (dtype_is_f32) {
+  if (headdim == 64)
+    hipLaunchKernelGGL((fwd_h16_kernel<64, ALIBI, T>), grid, dim3(FwdCfg<64>::NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_h16_kernel<128, ALIBI, T>), grid, dim3(FwdCfg<128>::NW * 64), 0, stream, p);
+}
+
+template <bool ALIBI>
+static void launch_forward_a(const FwdParams& p, int headdim, ElemType et, hipStream_t stream) {
+  const dim3 grid(p.B * p.H * p.nqb);
+  if (et == ElemType::kF32) {
     if (headdim == 64) hipLaunchKernelGGL((fwd_f32_kernel<64, ALIBI>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((fwd_f32_kernel<128, ALIBI>), grid, dim3(256), 0, stream, p);
+  } else if (et == ElemType::kF16) {
+    launch_forward_h16<ALIBI, _Float16>(p, headdim, stream);
   } else {
-    if (headdim == 64)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, ALIBI>), grid, dim3(FwdCfg<64>::NW * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, ALIBI>), grid, dim3(FwdCfg<128>::NW * 64), 0, stream, p);
+    launch_forward_h16<ALIBI, __bf16>(p, headdim, stream);
   }
 }
 
-hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream) {
-  if (p.alibi.slopes != nullptr) launch_forward_a<true>(p, headdim, dtype_is_f32, stream);
-  else launch_forward_a<false>(p, headdim, dtype_is_f32, stream);
+hipError_t launch_forward(FwdParams p, int headdim, ElemType et, hipStream_t stream) {
+  if (p.alibi.slopes != nullptr) launch_forward_a<true>(p, headdim, et, stream);
+  else launch_forward_a<false>(p, headdim, et, stream);
   return hipGetLastError();
 }
 

@@ -7,10 +7,13 @@
 
 namespace fa {
 
+// Element type of Q, K, V, O (and dO and the gradients in the backward).
+enum class ElemType { kBF16, kF32, kF16 };
+
 // Rows of the query block one forward work-group owns.
-int fwd_block_rows(int dtype_is_f32, int headdim);
+int fwd_block_rows(ElemType et, int headdim);
 // Enqueue the forward on `stream`; p.nqb must equal ceil(N / fwd_block_rows()).
-hipError_t launch_forward(FwdParams p, int headdim, int dtype_is_f32, hipStream_t stream);
+hipError_t launch_forward(FwdParams p, int headdim, ElemType et, hipStream_t stream);
 
 // fp8 (e4m3) forward: p.scale_log2 already holds softmax_scale * descale_q *
 // descale_k * log2(e); O is scaled by v_descale. p.nqb must equal
@@ -20,6 +23,6 @@ hipError_t launch_forward_fp8(FwdParams p, float v_descale, int headdim, hipStre
 
 // Backward: row statistic, then dK/dV (one pass over the queries per key
 // block) and dQ (one pass over the keys per query block).
-hipError_t launch_backward(BwdParams p, int headdim, int dtype_is_f32, hipStream_t stream);
+hipError_t launch_backward(BwdParams p, int headdim, ElemType et, hipStream_t stream);
 
 }  // namespace fa

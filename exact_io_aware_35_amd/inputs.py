@@ -32,7 +32,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str            # "f32", "bf16" or "fp8" (e4m3 bytes + a factor per tensor)
+    dtype: str            # "f32", "bf16", "f16" or "fp8" (e4m3 bytes + a factor per tensor)
     batch: int
     heads: int
     seqlen: int
@@ -78,7 +78,7 @@ WORKLOADS = {
 
 METRIC_WORKLOAD = "fwd_bf16_b2h8n4096d128"
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def make_inputs(w: Workload, seed: int = 0):

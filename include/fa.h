@@ -30,7 +30,8 @@
  *     [headdim] ([notes]); LSE and the backward's row statistic have layout
  *     [batch][heads][seqlen], fp32.
  *   - dtype selects the element type of Q, K, V, O, dO, dQ, dK, dV:
- *     FA_DTYPE_BF16 (bfloat16; MFMA with fp32 accumulation) or FA_DTYPE_F32.
+ *     FA_DTYPE_BF16 (bfloat16) or FA_DTYPE_F16 (IEEE half), both on MFMA with
+ *     fp32 accumulation, or FA_DTYPE_F32 (forward only).
  *     LSE is always fp32 (natural log). Outputs are rounded to nearest even.
  *   - Ownership: the caller owns every buffer, the workspace included. The
  *     library allocates and frees nothing and keeps no pointer after a call.
@@ -64,7 +65,7 @@
 extern "C" {
 #endif
 
-typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype_t;
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1, FA_DTYPE_F16 = 2 } fa_dtype_t;
 
 typedef enum {
   FA_OK = 0,
@@ -122,9 +123,11 @@ size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
  * The mask arguments must match the forward call that produced out and lse.
  * The result is deterministic: dQ is produced by its own pass over the keys
  * (no atomics), dK and dV by a pass over the queries.
+ * dtype is FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32 returns
+ * FA_ERR_UNSUPPORTED).
  * Precision: every product with P or dS as an operand takes fp16 operands
- * (Q, K and dO are converted from bf16, exactly for magnitudes in fp16's
- * normal range); Q, K and dO must lie below 65504 in magnitude.
+ * (bf16 Q, K and dO are converted, exactly for magnitudes in fp16's normal
+ * range); Q, K and dO must lie below 65504 in magnitude.
  */
 fa_status_t fa_backward(const void* q, const void* k, const void* v,
                         const void* out, const float* lse, const void* dout,
