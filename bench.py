@@ -161,6 +161,23 @@ def summarize(fetch_dir, write_dir, stats_dir, copy_mib, cmds):
     print(json.dumps(out, indent=1))
 
 
+def pretty_kernel(name):
+    """Readable form of this library's kernel names. The profiler leaves names
+    whose template arguments are the extended float types (__bf16, _Float16)
+    mangled; e.g. _ZN2fa14fwd_h16_kernelILi128ELb0EDF16bEEvNS_9FwdParamsE
+    becomes fa::fwd_h16_kernel<128, false, bf16>."""
+    import re
+    m = re.match(r"_ZN2fa(\d+)(\w+?)I(.*)EEvNS_\d+\w+E", name)
+    if not m or int(m.group(1)) != len(m.group(2)):
+        return name
+    args = re.findall(r"Li(\d+)E|Lb([01])E|DF16(b|_)", m.group(3))
+    out = []
+    for i, b, f in args:
+        out.append(i if i else ("true" if b == "1" else "false") if b else
+                   ("bf16" if f == "b" else "fp16"))
+    return f"fa::{m.group(2)}<{', '.join(out)}>"
+
+
 def stats_summary(stats_dir, workload, cmd):
     """Copy a rocprofv3 --stats table into profiles/kernel_stats_<workload>.txt."""
     import glob
@@ -182,10 +199,10 @@ def stats_summary(stats_dir, workload, cmd):
         f.write("\n".join(lines) + "\n\n")
         f.write("Steady state from the kernel trace (mean / median of the last 100 launches, us):\n")
         for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-            if "fa::" not in name:
+            if "fa::" not in name and not name.startswith("_ZN2fa"):
                 continue
             tail = sorted(d[-100:])
-            f.write(f"  {name}: mean {sum(tail) / len(tail) / 1e3:.2f}  "
+            f.write(f"  {pretty_kernel(name)}: mean {sum(tail) / len(tail) / 1e3:.2f}  "
                     f"median {tail[len(tail) // 2] / 1e3:.2f}  (launches {len(d)})\n")
 
 
@@ -212,9 +229,9 @@ def pmc_summary(dirs, workload):
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                if "fa::" not in r["Kernel_Name"]:
+                if "fa::" not in r["Kernel_Name"] and not r["Kernel_Name"].startswith("_ZN2fa"):
                     continue
-                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                vals.setdefault(pretty_kernel(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
     with open(os.path.join(ROOT, "profiles", f"pmc_{workload}.txt"), "w") as f:
         f.write(f"rocprofv3 counter summary of bench.py on {workload}: per kernel, the mean of "
