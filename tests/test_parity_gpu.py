@@ -475,3 +475,33 @@ def test_autograd_function_matches_direct_calls_and_oracle():
                             causal=True, seqlens_k=d["seqlens_k"].numpy())
     for name, got, want in zip(("dQ", "dK", "dV"), (q.grad, k.grad, v.grad), rg):
         assert_close(got.cpu(), want, TOL["bf16"]["grad"], name)
+
+
+def test_forward_and_backward_keep_memory_linear_in_n():
+    """The memory side of the method ([interview] section "Online Softmax":
+    the N x N score and probability matrices are never stored, so memory
+    drops from O(N^2) to O(N)): at N = 32768 a head's fp32 score matrix would
+    take 4 GiB, yet a forward into preallocated outputs and a backward with a
+    preallocated workspace leave the device's free memory exactly unchanged,
+    and the backward workspace grows linearly with N."""
+    B, H, N, D = 1, 2, 32768, 128
+    g = torch.Generator(device=DEV).manual_seed(0)
+    q, k, v, do = (torch.randn((B, N, H, D), generator=g, device=DEV).to(torch.bfloat16)
+                   for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(workspace_size(B, H, N, D), dtype=torch.uint8, device=DEV)
+    for _ in range(2):  # the first round loads code objects
+        forward(q, k, v, causal=True, out=o, lse=lse)
+        backward(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+        torch.cuda.synchronize()
+        free_before = torch.cuda.mem_get_info(DEV)[0]
+    forward(q, k, v, causal=True, out=o, lse=lse)
+    backward(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.cuda.mem_get_info(DEV)[0] == free_before
+    sizes = [workspace_size(B, H, n, D) for n in (4096, 8192, 16384, 32768)]
+    for a, b in zip(sizes, sizes[1:]):
+        assert abs(b / a - 2.0) < 0.01
+    assert sizes[-1] < 2 * 4 * B * H * N * D  # a few copies of the inputs, no N^2 term
