@@ -13,12 +13,18 @@
 //         exponent's scale, so the fp32 scores are exact sums of exact
 //         products;
 //   O^T += V^T P^T with P quantised to e4m3 (round to nearest even). P is
-//         taken as 2^(c2 s - M + 8) against a reference M that is never more
-//         than 0.8 (log2 units) below the running row max, so every P lies in
-//         [0, 2^8.8] (e4m3 tops out at 448) and P >= 2^-14 relative to the
-//         row max stays in e4m3's normal range. dv and 1 / l are applied in
-//         the epilogue; l sums the unrounded fp32 P, so the LSE does not
-//         see the quantisation.
+//         taken as 2^(c2 s - M + 3) against a reference M that is the exact
+//         running row max as of some earlier tile. A tile first uses the
+//         current M without computing its own max; only if some lane's sum
+//         of P exceeds 448 (e4m3's largest value, so one P might) is M raised
+//         to the exact running max, O and l rescaled, and the tile's P
+//         recomputed, each then at most 2^3. M starts at -1e30, so a row's
+//         first tile with a visible key takes that path. Skipping the max
+//         on the common path saves VALU work, which bounds this kernel. P
+//         below 2^-6 is rounded in e4m3's subnormal range, an absolute error
+//         of at most 2^-10 against a row sum l >= 2^3. dv and 1 / l are
+//         applied in the epilogue; l sums the unrounded fp32 P, so the LSE
+//         does not see the quantisation.
 //
 // Operand layouts (measured on gfx950): in the 32x32x64 fp8 MFMA lane l
 // supplies 32 bytes of row l % 32 of A (and of column l % 32 of B), and byte
@@ -93,14 +99,15 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-// Four waves (128 query rows) per work-group at both head dimensions: with
-// ~150 VGPRs three such work-groups fit on a CU, which measured faster than
-// eight-wave groups (two waves per SIMD) at D = 128.
+// Four waves (128 query rows) per work-group at both head dimensions, held
+// to at most 168 VGPRs (three waves per SIMD, so three such work-groups fit on
+// a CU; the cap costs one 4-byte spill outside the tile loop at D = 128).
+// This measured faster than eight-wave groups (two waves per SIMD).
 template <int D>
 using Fp8Shape = Fp8Cfg<D, 4>;
 
 template <int D>
-__global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) fwd_fp8_kernel(FwdParams p, float v_descale) {
+__global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(3))) fwd_fp8_kernel(FwdParams p, float v_descale) {
   using C = Fp8Shape<D>;
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];  // [buf][K | V]
 
@@ -192,7 +199,7 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) fwd_fp8_kernel(FwdParams
   f32x16_t oacc[C::DB];
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16_t{};
-  float m_ref = -INFINITY, l_part = 0.f;
+  float m_ref = -1e30f, l_part = 0.f;
   f32x16_t sacc[2];
   bool sact = false;
 
@@ -234,36 +241,40 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) fwd_fp8_kernel(FwdParams
     constexpr int buf = decltype(bufc)::value;
     const char* sv = smem + (2 * buf + 1) * C::TILE;
     if (!sact) return;
-    float mx = -INFINITY;
+    // Fast path without the tile max: P' = 2^(c2 S - M + 3) against the
+    // current M; if a lane's sum exceeds 448 (so possibly one P' does), redo
+    // the tile with M raised to the exact running max.
+    float acc = 0.f;
+    i32x8_t pb;
+    auto exps = [&](float mu) __attribute__((always_inline)) {
+      acc = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    const float mt = half_max(mx) * p.scale_log2;
-    // Raise M (to the exact running max) only when some row's tile max is
-    // more than 0.8 above it; O and l are rescaled to the new M.
-    if (__builtin_amdgcn_readfirstlane(__ballot(!(mt <= m_ref + 0.8f)) != 0)) {
-      const float m_new = fmaxf(m_ref, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
+        for (int i = 0; i < 16; i += 4) {
+          const float p0 = exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -mu));
+          const float p1 = exp2_fast(fmaf(sacc[kb][i + 1], p.scale_log2, -mu));
+          const float p2 = exp2_fast(fmaf(sacc[kb][i + 2], p.scale_log2, -mu));
+          const float p3 = exp2_fast(fmaf(sacc[kb][i + 3], p.scale_log2, -mu));
+          acc += (p0 + p1) + (p2 + p3);
+          pb[4 * kb + (i >> 2)] = pack_fp8x4(p0, p1, p2, p3);
+        }
+    };
+    exps(m_ref - 3.f);
+    if (__builtin_amdgcn_readfirstlane(__ballot(!(acc <= 448.f)) != 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      const float m_new = fmaxf(m_ref, half_max(mx) * p.scale_log2);
+      const float alpha = exp2_fast(m_ref - m_new);
       l_part *= alpha;
 #pragma unroll
       for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
       m_ref = m_new;
+      exps(m_ref - 3.f);
     }
-    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref - 8.f;
-    float acc = 0.f;
-    i32x8_t pb;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        const float p0 = exp2_fast(fmaf(sacc[kb][i], p.scale_log2, -mu));
-        const float p1 = exp2_fast(fmaf(sacc[kb][i + 1], p.scale_log2, -mu));
-        const float p2 = exp2_fast(fmaf(sacc[kb][i + 2], p.scale_log2, -mu));
-        const float p3 = exp2_fast(fmaf(sacc[kb][i + 3], p.scale_log2, -mu));
-        acc += (p0 + p1) + (p2 + p3);
-        pb[4 * kb + (i >> 2)] = pack_fp8x4(p0, p1, p2, p3);
-      }
     l_part += acc;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d) {
@@ -297,6 +308,9 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) fwd_fp8_kernel(FwdParams
   }
 
   const int qi = wq0 + ln;
+  // The lane's half, taken afresh from the hardware lane id: keeping it live
+  // across the tile loop would cost a register the cap does not leave.
+  const int hfe = (int)__lane_id() >> 5;
   const float l = half_sum(l_part);
   const float inv = l > 0.f ? v_descale / l : 0.f;
   if (qi < N) {
@@ -305,14 +319,14 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) fwd_fp8_kernel(FwdParams
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = 32 * d + 8 * g + 4 * hf;
+        const int col = 32 * d + 8 * g + 4 * hfe;
         *(u32x2_t*)(orow + col) =
             u32x2_t{pack_bf16x2(oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv),
                     pack_bf16x2(oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv)};
       }
-    if (hf == 0)
+    if (hfe == 0)
       p.lse[((size_t)b * p.H + h) * N + qi] =
-          l > 0.f ? (m_ref - 8.f + log2_fast(l)) * 0.69314718055994531f : -INFINITY;
+          l > 0.f ? (m_ref - 3.f + log2_fast(l)) * 0.69314718055994531f : -INFINITY;
   }
 }
 

@@ -204,8 +204,11 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
  *   lse       out: [batch][heads][seqlen], fp32, natural log
  * The result is the attention of fa_forward over the dequantised inputs, with
  * one further rounding: the probabilities are rounded to e4m3 (nearest even)
- * before the product with V, at a scale where the row's largest probability
- * lies in [2^8, 2^8.8]. The LSE is computed from the unrounded probabilities.
+ * before the product with V, at a scale where each probability is at most
+ * 448 and the row's sum is at least 2^3 times its largest weight, so that one
+ * rounded probability errs by at most 2^-4 of its weight, or 2^-13 of the
+ * row's largest weight where it is subnormal. The LSE is computed from the
+ * unrounded probabilities.
  * Inputs must not hold NaN. seqlens_k, softmax_scale, causal, the window, the
  * conventions and the error behaviour are those of fa_forward (dtype is fixed
  * here); a (batch, head) slice of seqlen + 128 rows must span less than 2^31

@@ -125,15 +125,19 @@ def _two_key_error(m, ratio):
 
 
 def pin_bound_near_tight(m):
-    """Two cases where one rounding nearly reaches the bound. With P'_1 = 2^8:
-    P'_2 = 2^6 (1 + 1/16) is a tie that rounds to 2^6, an error of 2^-4 of
+    """Two cases where one rounding nearly reaches the bound. With P'_1 = 2^3:
+    P'_2 = 2^1 (1 + 1/16) is a tie that rounds to 2^1, an error of 2^-4 of
     the value below it (the relative term); P'_2 = 3 * 2^-10, in the
     subnormal range, is a tie that rounds to 2^-8, an error of 2^-10 (the
-    absolute term, which the relative term alone does not cover)."""
+    absolute term, which the relative term alone does not cover);
+    P'_2 = 2^-17 rounds to 0, an error of the whole weight w_2, far below
+    2^-13 w_max (the min in the absolute term)."""
     err, bnd = _two_key_error(m, 1.0625 / 4)
     ok = 0.9 * bnd <= err <= bnd
-    err, bnd = _two_key_error(m, 3 * 2.0 ** -18)
-    return bool(ok and 0.8 * bnd <= err <= bnd)
+    err, bnd = _two_key_error(m, 3 * 2.0 ** -13)
+    ok = ok and 0.8 * bnd <= err <= bnd
+    err, bnd = _two_key_error(m, 2.0 ** -20)
+    return bool(ok and 0.9 * bnd <= err <= bnd)
 
 
 PINS = [pin_decode_closed_form, pin_decode_torch, pin_round, pin_attention_closed_forms,
@@ -176,8 +180,11 @@ MUTANTS = {
     "subnormal_threshold": ("np.where(a < 2.0 ** -6, 2.0 ** -9", "np.where(a < 2.0 ** -7, 2.0 ** -9"),
     "no_descale_v": ("e4m3_decode(v8) * float(descale_v)", "e4m3_decode(v8)"),
     "bound_half": ("2.0 ** -4 * (w @ av)", "2.0 ** -5 * (w @ av)"),
-    "bound_no_subnormal_term": ("+ 2.0 ** -18 * (vis.astype(np.float64) @ av)", ""),
-    "rounded_unscaled": ("* 2.0 ** 8, 0.0)", ", 0.0)"),
+    "bound_no_subnormal_term": (" + np.minimum(w, 2.0 ** -13 * wmax) @ av", ""),
+    "bound_subnormal_without_min": ("np.minimum(w, 2.0 ** -13 * wmax) @ av",
+                                    "2.0 ** -13 * wmax * (w > 0) @ av"),
+    "rounded_unscaled": ("* 2.0 ** 3, 0.0)", ", 0.0)"),
+    "rounded_scale_8": ("* 2.0 ** 3, 0.0)", "* 2.0 ** 8, 0.0)"),
 }
 
 
