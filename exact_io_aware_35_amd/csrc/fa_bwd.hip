@@ -346,6 +346,14 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 
 // ---------------------------------------------------------------- dK, dV (wave pairs)
 
+// 4-byte direct-to-LDS buffer load: lane i's dword lands at lds + 4 i (zero
+// past the descriptor's end).
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voffset,
+                                                 int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voffset, soffset, 0, 0);
+}
+
 template <int D>
 struct KvPairCfg {
   static constexpr int NP = 4;                 // wave pairs per work-group, 32 keys each
@@ -372,6 +380,9 @@ struct KvPairCfg {
 // A work-group barrier between the two phases of a tile hands P over; the
 // MFMA work is the same as in the one-wave form. P crosses in fp16, the
 // precision of its own MFMA operand, so dS is formed from the P that dV uses.
+// Each wave needs only one of a row's two statistics (LSE2 for P, D for dS),
+// so a tile's statistics sit in LDS split by kind: one 16-byte read brings
+// four rows' worth of the one a wave uses.
 template <int D, bool ALIBI, typename T>
 __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(BwdParams p) {
   using E = Elt16<T>;
@@ -451,9 +462,11 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
       buffer_load_lds16(qrsrc, sb + (wave * C::LPW + j) * 1024, loff[j], soff);
       buffer_load_lds16(orsrc, sb + C::TILE + (wave * C::LPW + j) * 1024, loff[j], soff);
     }
-    if (wave == 0)
-      buffer_load_lds16(srsrc, sb + 2 * C::TILE, lane * 16,
-                        __builtin_amdgcn_readfirstlane(t * C::BQ * 8));
+    if (wave == 0) {  // the tile's (LSE2, D) pairs, split: LSE2 of its 64 rows, then their D
+      const int so = __builtin_amdgcn_readfirstlane(t * C::BQ * 8);
+      buffer_load_lds4(srsrc, sb + 2 * C::TILE, lane * 8, so);
+      buffer_load_lds4(srsrc, sb + 2 * C::TILE + 4 * C::BQ, lane * 8 + 4, so);
+    }
   };
 
   int roff[C::DS];
@@ -505,12 +518,9 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
             for (int i = 0; i < 16; ++i)
               sa[i] = fmaf(fabsf(di + (float)(8 * (i >> 2) + (i & 3))), -slope_raw, sa[i]);
           }
-          f32x4_t st2[8];  // (LSE2, D) of rows 8 g + 4 hf + 2 u, +1 at st2[2 g + u]
+          f32x4_t l4[4];  // LSE2 of rows 8 g + 4 hf + (0..3) at l4[g]
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-              st2[2 * g + u] = *(const f32x4_t*)(st + 2 * (32 * qs + 8 * g + 4 * hf + 2 * u));
+          for (int g = 0; g < 4; ++g) l4[g] = *(const f32x4_t*)(st + 32 * qs + 8 * g + 4 * hf);
           if (EDGE && masked) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -520,9 +530,8 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
           }
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const f32x4_t r = st2[i >> 1];
-            const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -r[0]));
-            const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -r[2]));
+            const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
+            const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -l4[i >> 2][(i & 3) + 1]));
             pk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
           }
         }
@@ -554,12 +563,9 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
         u32x4_t dsk[C::KS];
 #pragma unroll
         for (int qs = 0; qs < C::QS; ++qs) {
-          f32x4_t st2[8];
+          f32x4_t d4[4];  // D of rows 8 g + 4 hf + (0..3) at d4[g]
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-              st2[2 * g + u] = *(const f32x4_t*)(st + 2 * (32 * qs + 8 * g + 4 * hf + 2 * u));
+          for (int g = 0; g < 4; ++g) d4[g] = *(const f32x4_t*)(st + C::BQ + 32 * qs + 8 * g + 4 * hf);
 #pragma unroll
           for (int hk = 0; hk < 2; ++hk) {
             const int ks = 2 * qs + hk;
@@ -568,9 +574,8 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
             for (int e = 0; e < 4; ++e) {
               const int i = 8 * hk + 2 * e;  // elements i, i + 1 of this qs
               const f16x8_t ph = __builtin_bit_cast(f16x8_t, pp);
-              const f32x4_t r = st2[i >> 1];
-              const float s0 = (float)ph[2 * e] * (pa[qs][i] - r[1]);
-              const float s1 = (float)ph[2 * e + 1] * (pa[qs][i + 1] - r[3]);
+              const float s0 = (float)ph[2 * e] * (pa[qs][i] - d4[i >> 2][i & 3]);
+              const float s1 = (float)ph[2 * e + 1] * (pa[qs][i + 1] - d4[i >> 2][(i & 3) + 1]);
               dsk[ks][e] = pack_f16x2(s0, s1);
             }
           }
