@@ -196,7 +196,12 @@ def stats_summary(stats_dir, workload, cmd):
                 "(forward and backward kernels)\n")
         f.write("command: " + cmd + "\n\n")
         f.write("Table from the --stats output (averages over every launch, warm-up included):\n")
-        f.write("\n".join(lines) + "\n\n")
+        rows = [r for r in lines[1:] if r.startswith('"_ZN2fa') or "fa::" in r.split('",')[0]]
+        f.write("\n".join(lines[:1] + rows) + "\n")
+        if len(lines) - 1 > len(rows):
+            f.write(f"({len(lines) - 1 - len(rows)} other kernels, from setting up the inputs, "
+                    "left out)\n")
+        f.write("\n")
         f.write("Steady state from the kernel trace (mean / median of the last 100 launches, us):\n")
         for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
             if "fa::" not in name and not name.startswith("_ZN2fa"):
