@@ -223,6 +223,11 @@ fa_status_t fa_forward_fp8(const void* q, const void* k, const void* v, void* ou
   if (!std::isfinite(scale_log2) || !(scale_log2 > 0.f))
     return fail(FA_ERR_INVALID_ARG, "softmax_scale * descale_q * descale_k is not a finite "
                 "positive fp32 value");
+  // |q . k| <= 448^2 headdim over e4m3 codes; the kernel needs every scaled
+  // score (log2 units) far inside fp32 range, above its -1e30 "no key yet" mark.
+  if ((double)scale_log2 * 448.0 * 448.0 * headdim > 0x1p64)
+    return fail(FA_ERR_INVALID_ARG, "softmax_scale * descale_q * descale_k is too large: "
+                "scaled scores could exceed 2^64");
   const void* ptrs[] = {q, k, v};
   for (int i = 0; i < 3; ++i)
     if ((s = check_ptr(ptrs[i], kQkvNames[i + 1])) != FA_OK) return s;

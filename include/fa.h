@@ -199,7 +199,10 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
  *                  the OCP e4m3 format (bias 7, 3 mantissa bits, subnormals,
  *                  0x7f / 0xff NaN, no infinities)
  *   descale_q, descale_k, descale_v : fp32 factors, finite and > 0; element x
- *                  of Q stands for e4m3(x) * descale_q, and likewise for K, V
+ *                  of Q stands for e4m3(x) * descale_q, and likewise for K, V;
+ *                  softmax_scale * descale_q * descale_k * log2(e) * 448^2 *
+ *                  headdim must not exceed 2^64 (every scaled score stays far
+ *                  inside fp32 range), else FA_ERR_INVALID_ARG
  *   out       out: [batch][seqlen][heads][headdim], bfloat16
  *   lse       out: [batch][heads][seqlen], fp32, natural log
  * The result is the attention of fa_forward over the dequantised inputs, with

@@ -192,6 +192,7 @@ def fwd_fp8(lib, **kw):
     (dict(dv=float("inf")), fb.FA_ERR_INVALID_ARG, "descale_v"),
     (dict(dv=-1.0), fb.FA_ERR_INVALID_ARG, "descale_v"),
     (dict(dq=1e30, dk=1e30), fb.FA_ERR_INVALID_ARG, "finite positive"),
+    (dict(dq=1e9, dk=1e9), fb.FA_ERR_INVALID_ARG, "too large"),
     (dict(scale=0.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
     (dict(D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
     (dict(B=0), fb.FA_ERR_INVALID_ARG, "batch"),
