@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = qb + 32 * qs + 8 * (i >> 2) + 4 * hf + (i & 3);
-          sa[i] = (row >= vqlo) & (row <= vqhi) ? sa[i] : -INFINITY;
+          sa[i] = ((row >= vqlo) & (row <= vqhi)) ? sa[i] : -INFINITY;
         }
       }
       // ALiBi: the exponent takes -slope log2(e) |i - j| (row i, key j).
@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int row = qb + 32 * qs + 8 * (i >> 2) + 4 * hf + (i & 3);
-              sa[i] = (row >= vqlo) & (row <= vqhi) ? sa[i] : -INFINITY;
+              sa[i] = ((row >= vqlo) & (row <= vqhi)) ? sa[i] : -INFINITY;
             }
           }
 #pragma unroll
@@ -784,7 +784,7 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = kt + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          sa[i] = (j >= lo) & (j <= hi) ? sa[i] : -INFINITY;
+          sa[i] = ((j >= lo) & (j <= hi)) ? sa[i] : -INFINITY;
         }
       }
 #pragma unroll

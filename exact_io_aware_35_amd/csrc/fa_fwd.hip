@@ -210,7 +210,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = jb + 32 * kb + 8 * (i >> 2) + (i & 3);
-            sacc[kb][qb][i] = (j >= lo) & (j <= hi) ? sacc[kb][qb][i] : -INFINITY;
+            sacc[kb][qb][i] = ((j >= lo) & (j <= hi)) ? sacc[kb][qb][i] : -INFINITY;
           }
       }
     }

@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_wa
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = jb + 16 * kb + i;
-          sacc[kb][i] = (j >= lo) & (j <= hi) ? sacc[kb][i] : -INFINITY;
+          sacc[kb][i] = ((j >= lo) & (j <= hi)) ? sacc[kb][i] : -INFINITY;
         }
     }
   };
