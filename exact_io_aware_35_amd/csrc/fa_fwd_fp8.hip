@@ -101,8 +101,7 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 
 // Four waves (128 query rows) per work-group at both head dimensions, held
 // to at most 168 VGPRs (three waves per SIMD, so three such work-groups fit on
-// a CU; the cap costs one 4-byte spill outside the tile loop at D = 128).
-// This measured faster than eight-wave groups (two waves per SIMD).
+// a CU). This measured faster than eight-wave groups (two waves per SIMD).
 template <int D>
 using Fp8Shape = Fp8Cfg<D, 4>;
 
