@@ -34,8 +34,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float scale,
                          int causal, int wl, int wr, fa_dtype_t dtype, int* wl_eff,
                          int* wr_eff, int row_mult = 1, int elem_bytes = 0) {
-  if (batch < 1 || heads < 1 || seqlen < 1)
-    return fail(FA_ERR_INVALID_ARG, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)",
+  if (batch < 0 || heads < 0 || seqlen < 0)
+    return fail(FA_ERR_INVALID_ARG, "batch, heads and seqlen must be >= 0 (got %d, %d, %d)",
                 batch, heads, seqlen);
   if (seqlen > (1 << 24))
     return fail(FA_ERR_INVALID_ARG, "seqlen %d exceeds 2^24", seqlen);
@@ -65,6 +65,10 @@ fa_status_t check_common(int batch, int heads, int seqlen, int headdim, float sc
   *wr_eff = causal ? 0 : (wr >= seqlen ? -1 : wr);
   return FA_OK;
 }
+
+// A call with no rows has nothing to compute: after its scalar arguments
+// pass, it returns FA_OK without reading any pointer or launching anything.
+bool empty_call(int batch, int heads, int seqlen) { return batch == 0 || heads == 0 || seqlen == 0; }
 
 fa_status_t check_ptr(const void* p, const char* name) {
   if (p == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is null", name);
@@ -162,6 +166,7 @@ fa_status_t fa_forward_ex(const void* q, const void* k, const void* v, int qkv_p
   fa_status_t s = check_common(batch, heads, seqlen, headdim, softmax_scale, causal,
                                window_left, window_right, dtype, &wl, &wr, qkv_packed ? 3 : 1);
   if (s != FA_OK) return s;
+  if (empty_call(batch, heads, seqlen)) return FA_OK;
   void* qkv[3];
   int rs_q;
   if ((s = resolve_qkv(q, k, v, qkv_packed, heads, headdim, dtype, kQkvNames, qkv, &rs_q)) !=
@@ -228,6 +233,7 @@ fa_status_t fa_forward_fp8(const void* q, const void* k, const void* v, void* ou
   if ((double)scale_log2 * 448.0 * 448.0 * headdim > 0x1p64)
     return fail(FA_ERR_INVALID_ARG, "softmax_scale * descale_q * descale_k is too large: "
                 "scaled scores could exceed 2^64");
+  if (empty_call(batch, heads, seqlen)) return FA_OK;
   const void* ptrs[] = {q, k, v};
   for (int i = 0; i < 3; ++i)
     if ((s = check_ptr(ptrs[i], kQkvNames[i + 1])) != FA_OK) return s;
@@ -281,6 +287,7 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
   if (s != FA_OK) return s;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
     return fail(FA_ERR_UNSUPPORTED, "the backward is built for bf16 and fp16 only");
+  if (empty_call(batch, heads, seqlen)) return FA_OK;
   void* qkv[3];
   int rs_q;
   if ((s = resolve_qkv(q, k, v, qkv_packed, heads, headdim, dtype, kQkvNames, qkv, &rs_q)) !=

@@ -49,10 +49,13 @@
  *     where L_b = seqlens_k[b] clamped to [0, seqlen] if seqlens_k is not NULL,
  *     else seqlen. A query row with no visible key gets O = 0, LSE = -inf and
  *     zero gradient contributions.
- *   - Supported sizes: headdim in {64, 128}; batch, heads, seqlen >= 1;
+ *   - Supported sizes: headdim in {64, 128}; batch, heads, seqlen >= 0;
  *     batch * heads * seqlen < 2^31 and seqlen <= 2^24; one (batch, head)
  *     slice, (seqlen + 128) * heads * headdim elements, below 2^31 bytes
  *     (else FA_ERR_UNSUPPORTED); softmax_scale finite and > 0.
+ *   - Empty calls: when batch, heads or seqlen is 0 and the scalar arguments
+ *     are valid, a call returns FA_OK at once. It reads no pointer (they may
+ *     be null), writes nothing and enqueues nothing.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

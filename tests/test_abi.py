@@ -55,9 +55,11 @@ def fwd(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status,needle", [
-    (dict(B=0), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(B=-1), fb.FA_ERR_INVALID_ARG, "batch"),
     (dict(H=-1), fb.FA_ERR_INVALID_ARG, "batch"),
-    (dict(N=0), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(N=-3), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(N=0, D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
+    (dict(B=0, scale=0.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
     (dict(N=(1 << 24) + 1), fb.FA_ERR_INVALID_ARG, "seqlen"),
     (dict(B=1 << 16, H=1 << 8, N=1 << 8), fb.FA_ERR_INVALID_ARG, "2^31"),
     (dict(D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
@@ -88,6 +90,23 @@ def bwd(lib, **kw):
                            a["dk"], a["dv"], a["seqlens"], a["B"], a["H"], a["N"], a["D"],
                            a["scale"], a["causal"], a["wl"], a["wr"], a["dtype"], a["ws"],
                            a["wsb"], None)
+
+
+@pytest.mark.parametrize("zero", [dict(B=0), dict(H=0), dict(N=0)])
+def test_empty_calls_return_ok_without_reading_pointers(zero):
+    """No rows, valid scalars: every entry point returns FA_OK with all its
+    pointers null (it must neither check nor read them)."""
+    lib = fb.load_library()
+    none = dict(q=None, k=None, v=None, out=None, lse=None)
+    assert fwd(lib, **none, **zero) == fb.FA_OK
+    assert fwd_fp8(lib, **none, **zero) == fb.FA_OK
+    assert bwd(lib, **none, dout=None, dq=None, dk=None, dv=None, ws=None, wsb=0,
+               **zero) == fb.FA_OK
+    assert lib.fa_backward_workspace_size(zero.get("B", 2), zero.get("H", 3), zero.get("N", 100),
+                                          64, fb.FA_DTYPE_BF16) == 0
+    # A bad scalar is still reported.
+    assert bwd(lib, **zero, dtype=fb.FA_DTYPE_F32) == fb.FA_ERR_UNSUPPORTED
+    assert fwd_fp8(lib, **zero, dq=0.0) == fb.FA_ERR_INVALID_ARG
 
 
 def test_workspace_size():
@@ -195,7 +214,7 @@ def fwd_fp8(lib, **kw):
     (dict(dq=1e9, dk=1e9), fb.FA_ERR_INVALID_ARG, "too large"),
     (dict(scale=0.0), fb.FA_ERR_INVALID_ARG, "softmax_scale"),
     (dict(D=96), fb.FA_ERR_UNSUPPORTED, "headdim"),
-    (dict(B=0), fb.FA_ERR_INVALID_ARG, "batch"),
+    (dict(B=-2), fb.FA_ERR_INVALID_ARG, "batch"),
     (dict(wl=-2), fb.FA_ERR_INVALID_ARG, "window"),
     (dict(q=None), fb.FA_ERR_INVALID_ARG, "q is null"),
     (dict(v=FAKE + 8), fb.FA_ERR_INVALID_ARG, "v is not 16-byte aligned"),

@@ -113,6 +113,23 @@ def test_forward_lengths(dtype, N):
     check_forward(d, dtype, causal=True)
 
 
+@pytest.mark.parametrize("shape", [(2, 0, 3, 64), (0, 40, 3, 128)], ids=["no-rows", "no-batch"])
+def test_empty_inputs_give_empty_outputs(shape):
+    """Zero rows: every call succeeds, launches nothing and returns outputs of
+    the right (empty) shapes."""
+    from exact_io_aware_35_amd import forward_fp8
+    dev = "cuda:0"
+    q, k, v, do = (torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    o, lse = forward(q, k, v, causal=True)
+    assert o.shape == shape and lse.shape == (shape[0], shape[2], shape[1])
+    dq, dk, dv = backward(q, k, v, o, lse, do, causal=True)
+    assert dq.shape == dk.shape == dv.shape == shape
+    b8 = torch.zeros(shape, dtype=torch.uint8, device=dev)
+    o8, lse8 = forward_fp8(b8, b8, b8, 1.0, 1.0, 1.0)
+    assert o8.shape == shape and lse8.shape == lse.shape
+    torch.cuda.synchronize()
+
+
 def test_forward_large_magnitude_and_scale():
     """Scores of magnitude ~1e2 (std-8 Q, K) exercise the max shift: without
     it exp would overflow fp32. V is scaled back to std 1 (exact: a power of
