@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd/bwd TFLOPS bf16 (B2 H8 N4096 D128) + % of MFMA peak, 1 MI355X"
 METRIC_WORKLOAD_NAME = "fwd_bf16_b2h8n4096d128"
 STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -- python bench.py "
-             "--workload {workload} --steps 200 --warmup 50 --no-cpu-baseline")
+             "--workload {workload} --steps 200 --warmup 500 --no-cpu-baseline")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "fp8": 5000.0}
 PEAK_HBM_GBS = 8000.0

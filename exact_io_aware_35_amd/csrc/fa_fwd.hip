@@ -172,21 +172,36 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
     const int kt = t * C::BN;
     sact = kt < wkhi && kt + C::BN > wklo;
     if (!sact) return;
-    // The 32-key blocks are independent accumulation chains; their MFMAs
-    // alternate so that each chain has a full MFMA of slack for its next
-    // operand read.
+    // The 32-key blocks are independent accumulation chains whose MFMAs
+    // alternate. The K operands are read PF d-steps ahead of their MFMAs; the
+    // scheduling barriers keep the compiler from sinking the reads back to
+    // one step ahead, where eight waves contending for LDS leave the read
+    // latency exposed (measured: 1.4% of the kernel at B2 H8 N4096 D128).
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = f32x16_t{};
+    constexpr int PF = 2;
+    vec8 kr[PF + 1][C::KB];
+    auto kread = [&](int s, int kb) { return *(const vec8*)(sk + kb * 32 * C::CPR * 16 + koff[s]); };
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s)
+    for (int s = 0; s < PF; ++s)
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const vec8 kop = *(const vec8*)(sk + kb * 32 * C::CPR * 16 + koff[s]);
+      for (int kb = 0; kb < C::KB; ++kb) kr[s][kb] = kread(s, kb);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) sacc[kb][qb] = E::mfma(kop, qf[qb][s], sacc[kb][qb]);
+    for (int s = 0; s < C::DS; ++s) {
+      if (s + PF < C::DS) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) kr[(s + PF) % (PF + 1)][kb] = kread(s + PF, kb);
       }
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+          sacc[kb][qb] = E::mfma(kr[s % (PF + 1)][kb], qf[qb][s], sacc[kb][qb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (ALIBI) {  // score of row i, key j: q.k - (slope / c) |i - j|
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
@@ -281,18 +296,29 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
     }
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) l_part[qb] += rsum[qb];
+    // O^T += V^T P^T: step i covers d-block i / KS and key step i % KS. The
+    // V^T operands are read VPF steps ahead, pinned like the K reads above.
+    constexpr int VPF = 2, NV = C::DB * C::KS;
+    auto vread = [&](int i) {
+      const char* vbase = sv + (i % C::KS) * 16 * C::CPR * 16;
+      const u32x2_t lo = lds_read_tr16(vbase + voff[i / C::KS][0]);
+      const u32x2_t hi = lds_read_tr16(vbase + voff[i / C::KS][1]);
+      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4_t vr[VPF + 1];
 #pragma unroll
-    for (int d = 0; d < C::DB; ++d)
+    for (int i = 0; i < VPF; ++i) vr[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const char* vbase = sv + ks * 16 * C::CPR * 16;
-        const u32x2_t lo = lds_read_tr16(vbase + voff[d][0]);
-        const u32x2_t hi = lds_read_tr16(vbase + voff[d][1]);
-        const u32x4_t a = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    for (int i = 0; i < NV; ++i) {
+      if (i + VPF < NV) vr[(i + VPF) % (VPF + 1)] = vread(i + VPF);
+      const int d = i / C::KS, ks = i % C::KS;
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
-          oacc[d][qb] = E::mfma(__builtin_bit_cast(vec8, a), __builtin_bit_cast(vec8, pk[qb][ks]), oacc[d][qb]);
-      }
+      for (int qb = 0; qb < C::QB; ++qb)
+        oacc[d][qb] = E::mfma(__builtin_bit_cast(vec8, vr[i % (VPF + 1)]),
+                              __builtin_bit_cast(vec8, pk[qb][ks]), oacc[d][qb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   using B0 = std::integral_constant<int, 0>;
