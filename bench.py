@@ -11,6 +11,7 @@ same shape's backward (timed separately, FLOPs counted as 2.5x the forward's).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --extra      # also write fwd/bwd lines for every workload
     python bench.py --copy-mib 256   # also run a plain 256 MiB device copy (counter calibration)
+    python bench.py --oracle-all 8   # host only: the fp64 oracle's rate on every workload
     python bench.py --summarize DIR_FETCH DIR_WRITE DIR_STATS   # write profiles/ summaries
 
 Only one GPU is used: --gpus N with N > 1 exits with a message.
@@ -297,6 +298,85 @@ def cpu_baseline(w, seconds):
                       f"query rows each, fp64 numpy; {dt:.1f} s"}
 
 
+def _visible_keys(w, kl, rows):
+    """Visible keys of each query row in ``rows`` (key length kl)."""
+    import numpy as np
+    r = np.asarray(rows, dtype=np.int64)
+    lo = np.zeros_like(r)
+    hi = np.full_like(r, kl - 1)
+    if w.causal:
+        hi = np.minimum(hi, r)
+    if w.window[0] >= 0:
+        lo = np.maximum(lo, r - w.window[0])
+    if w.window[1] >= 0:
+        hi = np.minimum(hi, r + w.window[1])
+    return np.clip(hi - lo + 1, 0, None)
+
+
+def oracle_rates(w, seconds):
+    """Rates of the fp64 oracle on workload w, one record per leg: the forward,
+    and the backward on workloads that have one. Each leg walks the (batch,
+    head) slices until about `seconds` of CPU time have passed. On workloads
+    whose oracle checks sampled query rows, the forward leg runs those rows
+    only. FLOPs follow the metric's count (4 B H N^2 D, halved for causal;
+    2.5x that for the backward); a sampled-row leg counts 4 D per visible
+    (row, key) pair."""
+    import numpy as np
+    import threadpoolctl
+    from exact_io_aware_35_amd.inputs import make_inputs
+    from oracle import attention_backward, attention_forward, attention_forward_rows
+    from oracle.fp8 import dequantise
+    d = make_inputs(w, 0)
+    if w.dtype == "fp8":
+        ds = d["descale"]
+        q, k, v = dequantise(d["q"].numpy(), d["k"].numpy(), d["v"].numpy(),
+                             ds["q"], ds["k"], ds["v"])
+    else:
+        q, k, v = (d[x].float().numpy() for x in ("q", "k", "v"))
+    sk = d["seqlens_k"].numpy() if d["seqlens_k"] is not None else None
+    do = d["dout"].float().numpy() if d["dout"] is not None else None
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    per_slice = fwd_flops(w) / (w.batch * w.heads)
+    legs = [("forward_rows" if w.sample_rows else "forward")]
+    if w.backward:
+        legs.append("backward")
+    out = []
+    for leg in legs:
+        done, flops, t0 = 0, 0.0, time.perf_counter()
+        for b in range(w.batch):
+            for h in range(w.heads):
+                sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
+                qs, ks, vs = (np.ascontiguousarray(x[sl]) for x in (q, k, v))
+                skb = None if sk is None else sk[b:b + 1]
+                kw = dict(softmax_scale=w.softmax_scale, causal=w.causal, window=w.window,
+                          seqlens_k=skb)
+                if leg == "forward":
+                    attention_forward(qs, ks, vs, **kw)
+                    flops += per_slice
+                elif leg == "forward_rows":
+                    rows = d["rows"][h].numpy()
+                    attention_forward_rows(qs, ks, vs, rows, **kw)
+                    kl = w.seqlen if skb is None else int(skb[0])
+                    flops += 4.0 * w.headdim * float(_visible_keys(w, kl, rows).sum())
+                else:
+                    attention_backward(qs, ks, vs, np.ascontiguousarray(do[sl]), **kw)
+                    flops += 2.5 * per_slice
+                done += 1
+                if time.perf_counter() - t0 > seconds:
+                    break
+            if time.perf_counter() - t0 > seconds:
+                break
+        dt = time.perf_counter() - t0
+        what = (f"{w.sample_rows + len(w.extra_rows)} sampled query rows of each slice"
+                if leg == "forward_rows" else f"all {w.seqlen} query rows of each slice")
+        out.append({"workload": w.name, "leg": leg, "value": round(flops / dt / 1e12, 6),
+                    "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                    "sample": f"{done} of {w.batch * w.heads} (batch, head) slices, {what}, "
+                              f"fp64 numpy; {dt:.1f} s"})
+    return out
+
+
 def run_workload(w, steps, warmup, backward=False, variant=None):
     """(fwd ms, bwd ms or None) for workload w on cuda:0. variant: None, "alibi"
     (the usual geometric slopes per head) or "qkvpacked" (one packed input)."""
@@ -352,6 +432,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true",
                     help="also time fwd/bwd of every workload; lines go to stderr")
+    ap.add_argument("--oracle-all", type=float, default=None, metavar="SECONDS",
+                    help="time the fp64 oracle on every workload (forward, backward where the "
+                         "workload has one; sampled rows for the long ones), each leg bounded "
+                         "by SECONDS of CPU time; prints one 'oracle:' JSON line per leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
@@ -363,6 +447,13 @@ def main():
                     help="write profiles/kernel_stats_WORKLOAD.txt from a --stats run of "
                          "bench.py --workload WORKLOAD")
     args = ap.parse_args()
+    if args.oracle_all is not None:
+        # Host-only: no GPU is touched.
+        from exact_io_aware_35_amd.inputs import WORKLOADS
+        for wk in WORKLOADS.values():
+            for rec in oracle_rates(wk, args.oracle_all):
+                print("oracle: " + json.dumps(rec), flush=True)
+        return
     if args.summarize:
         pmc = "rocprofv3 {opts} -- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-mib 256"
         summarize(*args.summarize, copy_mib=256,
