@@ -37,3 +37,11 @@ def test_oracle_rates_report_each_leg():
     w = Workload("t", "bf16", 1, 1, 128, 64, causal=True, sample_rows=5, extra_rows=(0, 127))
     (rec,) = bench.oracle_rates(w, 10.0)
     assert rec["leg"] == "forward_rows" and "7 sampled query rows" in rec["sample"]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
