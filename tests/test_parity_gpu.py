@@ -310,19 +310,21 @@ def _sample_rows(n, heads, count, seed):
     return torch.stack([torch.randperm(n, generator=g)[:count] for _ in range(heads)])
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["fwd_f32_b1h1n256d64"])
-def test_workload_small_full(name):
+def test_workload_small_full(name, seed):
     w = WORKLOADS[name]
-    d = make_inputs(w, 0)
+    d = make_inputs(w, seed)
     check_forward(d, w.dtype, w.causal, w.window, w.softmax_scale)
 
 
-def test_workload_b2h8n4096d128_sampled_rows():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_workload_b2h8n4096d128_sampled_rows(seed):
     w = WORKLOADS["fwd_bf16_b2h8n4096d128"]
-    d = make_inputs(w, 0)
+    d = make_inputs(w, seed)
     o, lse = gpu_forward(d, w.causal, w.window, w.softmax_scale)
     assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
-    d["rows"] = torch.cat([_sample_rows(4096, w.heads, 256, 99),
+    d["rows"] = torch.cat([_sample_rows(4096, w.heads, 256, 99 + seed),
                            torch.tensor([[0, 1, 4095]] * w.heads)], dim=1)
     _rows_compare(w, d, o, lse)
 
@@ -359,11 +361,13 @@ def test_backward_b2h8n4096d128_sampled_heads(causal):
                          f"{name}[b={b},h={h}]")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["fwd_bf16_b1h16n65536d128_causal",
                                   "fwd_bf16_b1h16n65536d128_window4096"])
-def test_workload_long_context_sampled_rows(name):
+def test_workload_long_context_sampled_rows(name, seed):
     w = WORKLOADS[name]
-    d = make_inputs(w, 0)
+    print(f"long context {name} seed {seed}", flush=True)
+    d = make_inputs(w, seed)
     o, lse = gpu_forward(d, w.causal, w.window, w.softmax_scale)
     _rows_compare(w, d, o, lse)
 
