@@ -105,6 +105,36 @@ def _dev_ptr(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name, shape, dtypes, device=None):
+    """Reject a caller-supplied tensor whose shape, dtype or device differs
+    from what the kernels read or write through its pointer (the C ABI sees
+    only the pointer, so a short buffer would be read or written past its
+    end)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise FaError(FA_ERR_INVALID_ARG,
+                      f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d) for d in dtypes)
+        raise FaError(FA_ERR_INVALID_ARG, f"{name} must be {want}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise FaError(FA_ERR_INVALID_ARG, f"{name} is on {t.device}, the inputs on {device}")
+
+
+def _check_forward_buffers(q, k, v, shape, out, lse, seqlens_k, out_dtypes, in_dtypes=None):
+    """Shapes, dtypes and device of a forward call's tensors (k, v None when
+    the input is packed). k and v must have q's dtype unless ``in_dtypes``
+    names the accepted ones."""
+    import torch
+    B, N, H, D = shape
+    for t, name in ((k, "k"), (v, "v")):
+        _expect(t, name, shape, in_dtypes or (q.dtype,), q.device)
+    _expect(out, "out", shape, out_dtypes, q.device)
+    _expect(lse, "lse", (B, H, N), (torch.float32,), q.device)
+    _expect(seqlens_k, "seqlens_k", (B,), (torch.int32,), q.device)
+
+
 def _alibi(alibi_slopes, batch, heads):
     """(pointer, batch stride) of optional ALiBi slopes: fp32 device [H] or [B, H]."""
     import torch
@@ -125,6 +155,7 @@ def _alibi(alibi_slopes, batch, heads):
 def _forward(q, k, v, packed, shape, causal, window, softmax_scale, seqlens_k, alibi_slopes,
              out, lse, stream):
     import torch
+    _check_forward_buffers(q, k, v, shape, out, lse, seqlens_k, (q.dtype,))
     lib = load_library()
     B, N, H, D = shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -182,6 +213,8 @@ def forward_fp8(q8, k8, v8, descale_q=1.0, descale_k=1.0, descale_v=1.0, causal=
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise FaError(FA_ERR_INVALID_ARG,
                           f"{name} must be torch.uint8 (e4m3 bytes) or torch.float8_e4m3fn")
+    _check_forward_buffers(q8, k8, v8, tuple(q8.shape), out, lse, seqlens_k, (torch.bfloat16,),
+                           (torch.uint8, torch.float8_e4m3fn))
     lib = load_library()
     B, N, H, D = q8.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -221,6 +254,10 @@ class PreparedCall:
 def prepare_forward(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_scale=None,
                     seqlens_k=None, stream=None):
     """forward() with every argument marshalled once; returns a callable."""
+    import torch
+    if out is None or lse is None:
+        raise FaError(FA_ERR_INVALID_ARG, "prepare_forward needs out and lse")
+    _check_forward_buffers(q, k, v, tuple(q.shape), out, lse, seqlens_k, (q.dtype,))
     lib = load_library()
     B, N, H, D = q.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -241,6 +278,10 @@ def prepare_forward_fp8(q8, k8, v8, out, lse, descale_q, descale_k, descale_v, c
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise FaError(FA_ERR_INVALID_ARG,
                           f"{name} must be torch.uint8 (e4m3 bytes) or torch.float8_e4m3fn")
+    if out is None or lse is None:
+        raise FaError(FA_ERR_INVALID_ARG, "prepare_forward_fp8 needs out and lse")
+    _check_forward_buffers(q8, k8, v8, tuple(q8.shape), out, lse, seqlens_k, (torch.bfloat16,),
+                           (torch.uint8, torch.float8_e4m3fn))
     lib = load_library()
     B, N, H, D = q8.shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -260,6 +301,15 @@ def workspace_size(batch, heads, seqlen, headdim, dtype_code=FA_DTYPE_BF16):
 def _backward(q, k, v, packed, shape, out, lse, dout, causal, window, softmax_scale, seqlens_k,
               alibi_slopes, grads, workspace, stream):
     import torch
+    _check_forward_buffers(q, k, v, shape, out, lse, seqlens_k, (q.dtype,))
+    if out is None or lse is None or dout is None:
+        raise FaError(FA_ERR_INVALID_ARG, "out, lse and dout are required")
+    _expect(dout, "dout", shape, (q.dtype,), q.device)
+    if packed:
+        _expect(grads[0], "dqkv", tuple(q.shape), (q.dtype,), q.device)
+    else:
+        for t, name in zip(grads, ("dq", "dk", "dv")):
+            _expect(t, name, shape, (q.dtype,), q.device)
     lib = load_library()
     B, N, H, D = shape
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -274,7 +324,8 @@ def _backward(q, k, v, packed, shape, out, lse, dout, causal, window, softmax_sc
                             _dev_ptr(grads[2], "dv"), _dev_ptr(seqlens_k, "seqlens_k"), slopes,
                             bstride, B, H, N, D, scale, int(bool(causal)), int(window[0]),
                             int(window[1]), code, _dev_ptr(workspace, "workspace"),
-                            workspace.numel(), _stream_handle(stream, q.device))
+                            workspace.numel() * workspace.element_size(),
+                            _stream_handle(stream, q.device))
     _check(lib, st)
 
 
