@@ -470,7 +470,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build measures the single-GPU kernel "
+        print("bench.py runs on exactly one GPU: it measures the single-GPU kernels "
               "(heads and batch shard across GPUs with no exchange); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
