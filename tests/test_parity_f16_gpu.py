@@ -111,3 +111,34 @@ def test_f16_workload_fwd_bwd_full(name):
     fwd_check(d, w.causal, w.window, w.softmax_scale)
     errs = bwd_check(d, w.causal, w.window, w.softmax_scale)
     print(name, {k: f"{v:.4g}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("name,count", [("fwd_bf16_b2h8n4096d128", 256),
+                                        ("fwd_bf16_b1h16n65536d128_causal", 0)])
+def test_f16_workload_sampled_rows(name, count):
+    """The metric shape and the 64K causal shape with fp16 inputs, at full size: every row
+    is computed on the GPU, and sampled rows are compared with the oracle."""
+    from oracle import attention_forward_rows
+    w = dataclasses.replace(WORKLOADS[name], dtype="f16")
+    print(f"f16 {name}", flush=True)
+    d = make_inputs(w, 0)
+    o, lse = forward(dev(d["q"]), dev(d["k"]), dev(d["v"]), causal=w.causal, window=w.window,
+                     softmax_scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    if count:  # workloads without their own row sample: seeded rows plus both ends
+        g = torch.Generator().manual_seed(7)
+        rows = torch.stack([torch.cat([torch.randperm(w.seqlen, generator=g)[:count],
+                                       torch.tensor([0, w.seqlen - 1])]) for _ in range(w.heads)])
+    else:
+        rows = d["rows"]
+    rows = rows.numpy()
+    ro, rl = attention_forward_rows(np64(d["q"]), np64(d["k"]), np64(d["v"]), rows,
+                                    w.softmax_scale, w.causal, w.window)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            r = rows[h]
+            assert_close(o[b, r, h, :], ro[b, h], TOL_O, f"O[b={b},h={h}]")
+            assert_lse(lse[b, h, r].numpy().astype(np.float64), rl[b, h], TOL_LSE)
