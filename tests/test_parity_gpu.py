@@ -526,3 +526,23 @@ def test_forward_and_backward_keep_memory_linear_in_n():
     for a, b in zip(sizes, sizes[1:]):
         assert abs(b / a - 2.0) < 0.01
     assert sizes[-1] < 2 * 4 * B * H * N * D  # a few copies of the inputs, no N^2 term
+
+
+def test_alibi_workload_b2h8n4096d128_sampled_rows():
+    """ALiBi (the usual per-head slopes) at the metric shape, full size, on sampled rows."""
+    w = WORKLOADS["fwd_bf16_b2h8n4096d128"]
+    d = make_inputs(w, 3)
+    slopes = geometric_slopes(w.heads)
+    o, lse = forward(dev(d["q"]), dev(d["k"]), dev(d["v"]), softmax_scale=w.softmax_scale,
+                     alibi_slopes=dev(slopes))
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    rows = torch.cat([_sample_rows(4096, w.heads, 128, 31),
+                      torch.tensor([[0, 2047, 4095]] * w.heads)], dim=1).numpy()
+    ro, rl = attention_forward_rows(np64(d["q"]), np64(d["k"]), np64(d["v"]), rows,
+                                    w.softmax_scale, alibi_slopes=slopes.numpy())
+    for b in range(w.batch):
+        for h in range(w.heads):
+            r = rows[h]
+            assert_close(o[b, r, h, :], ro[b, h], TOL["bf16"]["o"], f"O[b={b},h={h}]")
+            assert_lse(lse[b, h, r].numpy().astype(np.float64), rl[b, h], TOL["bf16"]["lse"])
