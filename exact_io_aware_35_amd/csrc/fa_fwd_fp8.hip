@@ -12,19 +12,21 @@
 //   S^T = K Q^T over raw bytes; the factor c * dq * dk is folded into the
 //         exponent's scale, so the fp32 scores are exact sums of exact
 //         products;
-//   O^T += V^T P^T with P quantised to e4m3 (round to nearest even). P is
-//         taken as 2^(c2 s - M + 3) against a reference M that is the exact
-//         running row max as of some earlier tile. A tile first uses the
-//         current M without computing its own max; only if some lane's sum
-//         of P exceeds 448 (e4m3's largest value, so one P might) is M raised
-//         to the exact running max, O and l rescaled, and the tile's P
-//         recomputed, each then at most 2^3. M starts at -1e30, so a row's
-//         first tile with a visible key takes that path. Skipping the max
-//         on the common path saves VALU work, which bounds this kernel. P
-//         below 2^-6 is rounded in e4m3's subnormal range, an absolute error
-//         of at most 2^-10 against a row sum l >= 2^3. dv and 1 / l are
-//         applied in the epilogue; l sums the unrounded fp32 P, so the LSE
-//         does not see the quantisation.
+//   O^T += V^T P^T with P quantised to e4m3 (round to nearest even). The
+//         library's accuracy contract (include/fa.h) lets each weight w
+//         enter as e4m3(c w) / c for any factor c with c w <= 448 and
+//         c w_max >= 1. Here P is taken as 2^(c2 s - M + 3) against a
+//         reference M that is the exact running row max as of some earlier
+//         tile, so c = 2^(3 + M_row - M) / w_max >= 2^3 / w_max: (ii) holds
+//         with room to spare. A tile first uses the current M without
+//         computing its own max; only if some lane's sum of P exceeds 448
+//         (e4m3's largest value, so one P might) is M raised to the exact
+//         running max, O and l rescaled, and the tile's P recomputed, each
+//         then at most 2^3, which keeps (i). M starts at -1e30, so a row's
+//         first tile with a visible key takes that path. Skipping the max on
+//         the common path saves VALU work, which bounds this kernel. dv and
+//         1 / l are applied in the epilogue; l sums the unrounded fp32 P, so
+//         the LSE does not see the quantisation.
 //
 // Operand layouts (measured on gfx950): in the 32x32x64 fp8 MFMA lane l
 // supplies 32 bytes of row l % 32 of A (and of column l % 32 of B), and byte

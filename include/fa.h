@@ -209,12 +209,15 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
  *   out       out: [batch][seqlen][heads][headdim], bfloat16
  *   lse       out: [batch][heads][seqlen], fp32, natural log
  * The result is the attention of fa_forward over the dequantised inputs, with
- * one further rounding: the probabilities are rounded to e4m3 (nearest even)
- * before the product with V, at a scale where each probability is at most
- * 448 and the row's sum is at least 2^3 times its largest weight, so that one
- * rounded probability errs by at most 2^-4 of its weight, or 2^-13 of the
- * row's largest weight where it is subnormal. The LSE is computed from the
- * unrounded probabilities.
+ * one further rounding, which the fp8 P V product forces: each softmax weight
+ * w (an exact probability of the row) enters that product as e4m3(c w) / c,
+ * rounded to nearest even, for factors c > 0 (which may differ between the
+ * row's key tiles) with c w <= 448 for every weight rounded with it and
+ * c w_max >= 1, w_max the row's largest weight. From the e4m3 format alone
+ * (relative spacing 2^-3 above 2^-6, absolute spacing 2^-9 below), each
+ * weight then moves by at most max(2^-4 w, min(w, 2^-10 w_max)), and each
+ * output element by at most the sum over keys of that times |v|. The LSE is
+ * computed from the unrounded probabilities.
  * Inputs must not hold NaN. seqlens_k, softmax_scale, causal, the window, the
  * conventions and the error behaviour are those of fa_forward (dtype is fixed
  * here); a (batch, head) slice of seqlen + 128 rows must span less than 2^31

@@ -12,38 +12,44 @@ the plainest reading:
   is exact) over the dequantised values. ``attention_forward_fp8`` is that
   exact attention: the definitions of ``attention.py`` applied to the decoded
   inputs, in fp64.
-* The one further rounding the fp8 product forces is that of P: the P V
-  product runs on fp8 operands, so P is rounded to e4m3 (to nearest, ties to
-  even) as P' = 2^(x - M + 3), M the tile's reference max (below). The LSE is
-  computed from the unrounded P. ``fp8_output_bound`` bounds the effect.
+* The one further rounding an fp8 P V product forces is that of the
+  probabilities, which must enter it as e4m3 values. The contract: the
+  softmax weight w_j of key j (the exact probability, sum_j w_j = 1) enters as
+  e4m3(c w_j) / c, rounded to nearest (ties to even), for some factor c > 0
+  that may differ between groups of keys of a row, under two conditions:
+    (i)  c w_j <= 448 for every weight rounded with it (nothing saturates);
+    (ii) c w_max >= 1, w_max the row's largest weight.
+  The LSE is computed from the unrounded weights. ``fp8_output_bound`` bounds
+  what this rounding can do to O; it depends on the format and on (i), (ii)
+  only, not on how an implementation picks c.
 
 e4m3 (OCP): sign bit, 4 exponent bits with bias 7, 3 mantissa bits. Exponent
 field 0 holds subnormals m * 2^-9; exponent field e > 0 holds (1 + m/8) 2^(e-7);
 the two codes with all exponent and mantissa bits set (0x7f, 0xff) are NaN;
 there are no infinities; the largest finite magnitude is 448.
 
-The bound. Let P'_j = 2^(x_j - M + 3) be the kernel's probability of key j at
-the reference M of its tile (x_j the score in log2 units). M is only ever set
-to the exact running max of the scores seen so far, and every P'_j <= 448 (a
-tile whose per-lane sum of P' exceeds 448 is redone against a raised M). Let
-P^_j be the e4m3 rounding of P'_j. Round-to-nearest gives
-|P^_j - P'_j| <= 2^-4 P'_j where P'_j is in the normal range (>= 2^-6), and at
-most min(P'_j, 2^-10) below it (half the subnormal step, or the value itself
-when it rounds to 0). Each tile's contribution is later multiplied by
-alpha = 2^(M - M_final) <= 1, and O is divided by l = sum_j alpha P'_j. M_final
-is the score of some key, whose term is 2^3, so l >= 2^3 sum_j 2^(x_j - x_max)
-= 2^3 / w_max. With w_j = alpha P'_j / l the exact softmax weights,
+The bound. Let y = c w be a value rounded to e4m3, 0 <= y <= 448 by (i).
+Normal range (y >= 2^-6): y lies in [2^e, 2^(e+1)) with e >= -6, where the
+spacing is 2^(e-3), so rounding to nearest errs by at most 2^(e-4) <= 2^-4 y.
+Subnormal range (y < 2^-6): the spacing is 2^-9, so the error is at most half
+of it, 2^-10; and a value at or below 2^-10 rounds to 0, erring by y itself.
+In both ranges, |e4m3(y) - y| <= max(2^-4 y, min(y, 2^-10)) (in the normal
+range the second term is 2^-10 <= 2^-4 y; in the subnormal range the first is
+below the second). Dividing by c, and using 1/c <= w_max from (ii), the weight
+of key j moves by at most max(2^-4 w_j, min(w_j, 2^-10 w_max)). O is the sum
+of the weights times V, so per output element
 
-    |O_fp8 - O| <= 2^-4 sum_j w_j |v_j| + sum_j min(w_j, 2^-13 w_max) |v_j|
+    |O_fp8 - O| <= sum_j max(2^-4 w_j, min(w_j, 2^-10 w_max)) |v_j|
 
-per output element (v the dequantised V, the sums over visible keys). The kernel's other roundings (fp32
-scores from exact products, the fp32 exponential, the bf16 output) are far
-smaller or are bounded separately by the tests.
+(v the dequantised V, the sums over visible keys). An implementation's other
+roundings (fp32 scores from exact products, the fp32 exponential, the bf16
+output) are bounded separately by the tests that use this.
 
 Parity of this module: pinned by tests/test_oracle_fp8.py (the decoder against
 the format's closed-form values and torch's float8_e4m3fn, the rounding's ties,
-closed forms of the attention, and the bound against a simulation of the
-rounding it bounds).
+closed forms of the attention, and the bound against simulations of the
+rounding it bounds at several scales the contract allows, some of them
+reaching it).
 """
 
 from __future__ import annotations
@@ -78,7 +84,7 @@ def e4m3_decode(codes):
 def e4m3_round(x):
     """Nearest e4m3 value of each x (ties to even), as float64.
 
-    Magnitudes above 448 (which the forward never produces) raise ValueError.
+    Magnitudes above 448 (excluded by condition (i)) raise ValueError.
     """
     x = np.asarray(x, dtype=np.float64)
     a = np.abs(x)
@@ -121,8 +127,9 @@ def _weights(qh, kh, scale, vis):
 
 def fp8_output_bound(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale=None,
                      causal=False, window=(-1, -1), seqlens_k=None, rows=None):
-    """Per-element bound on |O_fp8 - O_exact| from rounding P to e4m3 (module notes):
-    2^-4 sum_j w_ij |v_jd| + sum_j min(w_ij, 2^-13 max_j w_ij) |v_jd|.
+    """Per-element bound on |O_fp8 - O_exact| from rounding the weights to
+    e4m3 under the contract of the module notes:
+    sum_j max(2^-4 w_ij, min(w_ij, 2^-10 max_k w_ik)) |v_jd|.
 
     Returns [B,N,H,D], or [B,H,R,D] for the query rows ``rows`` ([H, R] or [R]).
     """
@@ -142,9 +149,9 @@ def fp8_output_bound(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale=
             r = np.arange(N) if rows is None else rows[h]
             vis = visible_mask(len(r), N, causal, window[0], window[1], kl, q_pos=r)
             w = _weights(q[b, r, h, :], k[b, :, h, :], scale, vis)
-            av = np.abs(v[b, :, h, :])
             wmax = w.max(axis=1, keepdims=True)
-            bound = 2.0 ** -4 * (w @ av) + np.minimum(w, 2.0 ** -13 * wmax) @ av
+            per_key = np.maximum(2.0 ** -4 * w, np.minimum(w, 2.0 ** -10 * wmax))
+            bound = per_key @ np.abs(v[b, :, h, :])
             if rows is None:
                 out[b, :, h, :] = bound
             else:
@@ -154,10 +161,20 @@ def fp8_output_bound(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale=
 
 def attention_forward_fp8_rounded(q8, k8, v8, descale_q, descale_k, descale_v,
                                   softmax_scale=None, causal=False, window=(-1, -1),
-                                  seqlens_k=None):
-    """O with P rounded to e4m3 at the final reference: P' = 2^3 P / max_j P
-    (row max -> 2^3), O = sum_j e4m3(P'_j) v_j / sum_j P'_j. One instance of the
-    rounding ``fp8_output_bound`` covers (the tests use it to check the bound)."""
+                                  seqlens_k=None, top=1.0, key_block=None):
+    """O with the weights rounded to e4m3 as the contract allows: weight w_j
+    enters as e4m3(c w_j) / c. One instance of the rounding
+    ``fp8_output_bound`` covers, for checking that bound.
+
+    Choice of c: with ``key_block`` None, one factor per row that maps the
+    row's largest weight to ``top`` (1 <= top <= 448, the range conditions (i)
+    and (ii) allow). With ``key_block`` = n, one factor per row and block of
+    n consecutive keys, mapping the block's largest weight to 448: the largest
+    factor (i) allows for that block, and c w_max >= 448 w_max / (block max)
+    >= 448 satisfies (ii).
+    """
+    if not 1.0 <= top <= E4M3_MAX:
+        raise ValueError("top must lie in [1, 448]")
     q, k, v = dequantise(q8, k8, v8, descale_q, descale_k, descale_v)
     B, N, H, D = q.shape
     scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -165,11 +182,18 @@ def attention_forward_fp8_rounded(q8, k8, v8, descale_q, descale_k, descale_v,
     for b in range(B):
         vis = visible_mask(N, N, causal, window[0], window[1], _key_len(seqlens_k, b, N))
         for h in range(H):
-            s = np.where(vis, scale * (q[b, :, h, :] @ k[b, :, h, :].T), -np.inf)
-            m = s.max(axis=1)
-            fin = np.isfinite(m)
-            pp = np.where(fin[:, None], np.exp(s - np.where(fin, m, 0.0)[:, None]) * 2.0 ** 3, 0.0)
-            l = pp.sum(axis=1)
-            num = e4m3_round(pp) @ v[b, :, h, :]
-            out[b, :, h, :] = np.where(fin[:, None], num / np.where(fin, l, 1.0)[:, None], 0.0)
+            w = _weights(q[b, :, h, :], k[b, :, h, :], scale, vis)
+            if key_block is None:
+                ref = np.broadcast_to(w.max(axis=1, keepdims=True), w.shape)
+                target = top
+            else:
+                starts = np.arange(0, N, key_block)
+                ref = np.repeat(np.maximum.reduceat(w, starts, axis=1),
+                                np.diff(np.append(starts, N)), axis=1)
+                target = E4M3_MAX
+            c = np.where(ref > 0, target / np.where(ref > 0, ref, 1.0), 1.0)
+            # c w can exceed the target by one fp64 rounding; the clip removes
+            # only that excess.
+            y = np.minimum(c * w, target)
+            out[b, :, h, :] = (e4m3_round(y) / c) @ v[b, :, h, :]
     return out

@@ -3,9 +3,11 @@
 The e4m3 decoder is checked against the format's closed-form values and
 against torch's float8_e4m3fn conversion over all 256 codes; the rounding
 against torch's conversion and its ties; the attention over decoded inputs
-against closed forms; the bound on P's rounding against a simulation of that
-rounding, with cases that bring the simulated error close to the bound. A
-planted mistake in a copy of the module fails at least one pin.
+against closed forms; the bound on P's rounding against simulations of that
+rounding at several factors the contract allows (the row's largest weight
+mapped to 1, 8 or 448, or each key block's largest weight mapped to 448), with
+cases that bring the simulated error to the bound. A planted mistake in a copy
+of the module fails at least one pin.
 """
 
 import math
@@ -90,26 +92,33 @@ def pin_attention_closed_forms(m):
 
 
 def pin_bound_covers_rounding(m):
+    """The bound covers the rounding at every scale the contract allows that
+    is tried here: the row's largest weight mapped to 1 (the smallest factor
+    (ii) allows), to 8 and to 448 (the largest (i) allows), and one factor per
+    block of 16 keys mapping each block's largest weight to 448."""
     ok = True
     worst = 0.0
+    scales = [dict(top=1.0), dict(top=8.0), dict(top=448.0), dict(key_block=16)]
     for seed, mask, std in [(3, dict(), 1.0), (4, dict(causal=True), 2.0),
                             (5, dict(window=(5, 3)), 1.0), (6, dict(seqlens_k=[17]), 4.0)]:
         q8, k8, v8 = _case(seed=seed, std=std)
         args = (q8, k8, v8, 1 / 32, 1 / 32, 1 / 32)
         o, _ = m.attention_forward_fp8(*args, **mask)
-        r = m.attention_forward_fp8_rounded(*args, **mask)
         bnd = m.fp8_output_bound(*args, **mask)
-        err = np.abs(r - o)
-        ok &= bool((err <= bnd + 1e-15).all())
-        worst = max(worst, float((err / (bnd + 1e-300)).max()))
+        for sc in scales:
+            r = m.attention_forward_fp8_rounded(*args, **mask, **sc)
+            err = np.abs(r - o)
+            ok &= bool((err <= bnd + 1e-15).all())
+            worst = max(worst, float((err / (bnd + 1e-300)).max()))
     return ok and worst > 0.05
 
 
-def _two_key_error(m, ratio):
+def _two_key_error(m, ratio, top=1.0):
     """Query row 1 of a two-key case sees scores 0 and ln(ratio), V rows 0 and
-    (1, 1, ...): returns (|O_rounded - O_exact|, bound) of its first element.
-    The scores are realised with decoded Q = (1, 0, ...), K rows 0 and
-    (ln ratio, 0, ...) (one e4m3 code -1 with descale_k = -ln ratio)."""
+    (1, 1, ...): returns (|O_rounded - O_exact|, bound) of its first element,
+    with the larger weight mapped to ``top``. The scores are realised with
+    decoded Q = (1, 0, ...), K rows 0 and (ln ratio, 0, ...) (one e4m3 code
+    -1 with descale_k = -ln ratio)."""
     s2 = math.log(ratio)
     q8 = np.zeros((1, 2, 1, 16), np.uint8)
     k8 = np.zeros((1, 2, 1, 16), np.uint8)
@@ -119,29 +128,49 @@ def _two_key_error(m, ratio):
     v8[0, 1, 0, :] = codes_of([1.0])[0]
     args = (q8, k8, v8, 1.0, -s2, 1.0)
     o, _ = m.attention_forward_fp8(*args, softmax_scale=1.0)
-    r = m.attention_forward_fp8_rounded(*args, softmax_scale=1.0)
+    r = m.attention_forward_fp8_rounded(*args, softmax_scale=1.0, top=top)
     bnd = m.fp8_output_bound(*args, softmax_scale=1.0)
     return abs(r[0, 1, 0, 0] - o[0, 1, 0, 0]), bnd[0, 1, 0, 0]
 
 
 def pin_bound_near_tight(m):
-    """Two cases where one rounding nearly reaches the bound. With P'_1 = 2^3:
-    P'_2 = 2^1 (1 + 1/16) is a tie that rounds to 2^1, an error of 2^-4 of
-    the value below it (the relative term); P'_2 = 3 * 2^-10, in the
-    subnormal range, is a tie that rounds to 2^-8, an error of 2^-10 (the
-    absolute term, which the relative term alone does not cover);
-    P'_2 = 2^-17 rounds to 0, an error of the whole weight w_2, far below
-    2^-13 w_max (the min in the absolute term)."""
+    """Cases where one rounding reaches, or nearly reaches, the bound, with the
+    larger weight w_1 mapped to 1 (c = 1 / w_1, the smallest factor the
+    contract allows), so the smaller one is rounded at y = ratio:
+    y = 2^-2 (1 + 1/16) is a tie that rounds to 2^-2, an error of 2^-4 of the
+    value below it (the relative term, 94% of the bound);
+    y = 3 * 2^-10, in the subnormal range, is a tie that rounds to 2^-8, an
+    error of 2^-10 w_1 (the absolute term, all of the bound; the relative
+    term alone gives 3/16 of it);
+    y = 2^-17 rounds to 0, an error of the whole weight w_2, far below
+    2^-10 w_1 (the min in the absolute term, all of the bound).
+    A larger factor makes the same subnormal rounding smaller against the
+    weight: with w_1 mapped to 8, a ratio of 3 * 2^-13 is rounded at
+    y = 3 * 2^-10 and errs by 2^-10 / c = 2^-13 w_1, a third of the bound
+    (which is w_2 = 3 * 2^-13 w_1 there)."""
     err, bnd = _two_key_error(m, 1.0625 / 4)
     ok = 0.9 * bnd <= err <= bnd
-    err, bnd = _two_key_error(m, 3 * 2.0 ** -13)
-    ok = ok and 0.8 * bnd <= err <= bnd
-    err, bnd = _two_key_error(m, 2.0 ** -20)
-    return bool(ok and 0.9 * bnd <= err <= bnd)
+    err, bnd = _two_key_error(m, 3 * 2.0 ** -10)
+    ok = ok and 0.99 * bnd <= err <= bnd
+    err, bnd = _two_key_error(m, 2.0 ** -17)
+    ok = ok and 0.99 * bnd <= err <= bnd
+    err, bnd = _two_key_error(m, 3 * 2.0 ** -13, top=8.0)
+    return bool(ok and abs(err / bnd - 1 / 3) < 1e-9)
+
+
+def pin_rounded_rejects_scales_outside_contract(m):
+    for top in (0.5, 449.0):
+        try:
+            q8, k8, v8 = _case(n=4, seed=8)
+            m.attention_forward_fp8_rounded(q8, k8, v8, 1 / 32, 1 / 32, 1 / 32, top=top)
+        except ValueError:
+            continue
+        return False
+    return True
 
 
 PINS = [pin_decode_closed_form, pin_decode_torch, pin_round, pin_attention_closed_forms,
-        pin_bound_covers_rounding, pin_bound_near_tight]
+        pin_bound_covers_rounding, pin_bound_near_tight, pin_rounded_rejects_scales_outside_contract]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -179,12 +208,16 @@ MUTANTS = {
     "normal_step": ("np.exp2(ex - 3.0)", "np.exp2(ex - 2.0)"),
     "subnormal_threshold": ("np.where(a < 2.0 ** -6, 2.0 ** -9", "np.where(a < 2.0 ** -7, 2.0 ** -9"),
     "no_descale_v": ("e4m3_decode(v8) * float(descale_v)", "e4m3_decode(v8)"),
-    "bound_half": ("2.0 ** -4 * (w @ av)", "2.0 ** -5 * (w @ av)"),
-    "bound_no_subnormal_term": (" + np.minimum(w, 2.0 ** -13 * wmax) @ av", ""),
-    "bound_subnormal_without_min": ("np.minimum(w, 2.0 ** -13 * wmax) @ av",
-                                    "2.0 ** -13 * wmax * (w > 0) @ av"),
-    "rounded_unscaled": ("* 2.0 ** 3, 0.0)", ", 0.0)"),
-    "rounded_scale_8": ("* 2.0 ** 3, 0.0)", "* 2.0 ** 8, 0.0)"),
+    "bound_half": ("np.maximum(2.0 ** -4 * w,", "np.maximum(2.0 ** -5 * w,"),
+    "bound_no_subnormal_term": ("np.maximum(2.0 ** -4 * w, np.minimum(w, 2.0 ** -10 * wmax))",
+                                "2.0 ** -4 * w"),
+    "bound_subnormal_without_min": ("np.minimum(w, 2.0 ** -10 * wmax))",
+                                    "2.0 ** -10 * wmax * (w > 0))"),
+    "bound_subnormal_tighter": ("np.minimum(w, 2.0 ** -10 * wmax))", "np.minimum(w, 2.0 ** -13 * wmax))"),
+    "rounded_unscaled": ("(e4m3_round(y) / c) @", "(e4m3_round(y)) @"),
+    "rounded_no_rounding": ("(e4m3_round(y) / c) @", "(y / c) @"),
+    "rounded_top_ignored": ("target = top\n", "target = 8.0\n"),
+    "rounded_no_range_check": ("if not 1.0 <= top <= E4M3_MAX:", "if False:"),
 }
 
 
