@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd/bwd TFLOPS bf16 (B2 H8 N4096 D128) + % of MFMA peak, 1 MI355X"
 METRIC_WORKLOAD_NAME = "fwd_bf16_b2h8n4096d128"
 STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -- python bench.py "
-             "--workload {workload} --steps 200 --warmup 500 --no-cpu-baseline")
+             "--workload {workload} --steps 200 --warmup 500 --no-cpu-baseline --no-clock")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "fp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
@@ -93,6 +93,75 @@ def per_launch_ms(fn, launches):
     torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in evs)
     return t[len(t) // 2], sum(t) / len(t), t[0]
+
+
+MI355X_CUS = 256
+BF16_FLOP_PER_CLK_PER_CU = 4096   # dense 32x32x16 bf16 MFMA rate: 2.5 PF/s at 2.4 GHz
+
+
+def sample_gfx_clock(fn, seconds=0.6, period_s=0.004):
+    """Shader clock while fn() runs back to back for about `seconds`.
+
+    The GPU's own telemetry is read through amdsmi from a host thread while
+    the launches run: the gpu_metrics table's per-XCD current graphics clocks
+    (falling back to the driver's current GFX clock). Returns a dict with the
+    median over the samples and how it was read, or None with a reason if the
+    telemetry is not readable here."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # noqa: BLE001 - report, never fail the bench on telemetry
+        return {"mhz": None, "why": f"amdsmi unavailable: {type(e).__name__}: {e}"[:200]}
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))
+                  and 0 < c < 10000]
+            if xs:
+                return sum(xs) / len(xs), "gpu_metrics current_gfxclks (mean over XCDs)"
+        except Exception:  # noqa: BLE001
+            pass
+        c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+        return float(c["clk"]), "amdsmi_get_clock_info GFX clk"
+
+    samples, src, stop = [], [None], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                v, src[0] = read()
+                samples.append(v)
+            except Exception:  # noqa: BLE001
+                pass
+            stop.wait(period_s)
+
+    for _ in range(50):  # clock up before sampling starts
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=2.0)
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    if not samples:
+        return {"mhz": None, "why": "no telemetry sample could be read"}
+    samples.sort()
+    return {"mhz": samples[len(samples) // 2], "samples": len(samples),
+            "min_mhz": samples[0], "max_mhz": samples[-1], "source": src[0],
+            "how": f"sampled every {period_s * 1e3:.0f} ms from a host thread while the "
+                   f"forward ran back to back for {seconds:.1f} s"}
 
 
 def load_traffic():
@@ -223,7 +292,7 @@ PMC_PASSES = [
     "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SMEM SQ_INSTS_BRANCH SQ_WAVES",
 ]
 PMC_CMD = ("rocprofv3 --pmc {counters} --output-format csv -- python bench.py --workload "
-           "{workload} --steps 5 --warmup 1 --no-cpu-baseline")
+           "{workload} --steps 5 --warmup 1 --no-cpu-baseline --no-clock")
 
 
 def pmc_summary(dirs, workload):
@@ -292,8 +361,10 @@ def cpu_baseline(w, seconds):
         if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
+    import torch
     return {"value": round(done * flops_per_head / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "torch_threads": torch.get_num_threads(),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{done} of {w.batch * w.heads} (batch, head) slices, all {w.seqlen} "
                       f"query rows each, fp64 numpy; {dt:.1f} s"}
 
@@ -430,6 +501,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock (amdsmi) after the timed region")
     ap.add_argument("--extra", action="store_true",
                     help="also time fwd/bwd of every workload; lines go to stderr")
     ap.add_argument("--oracle-all", type=float, default=None, metavar="SECONDS",
@@ -455,7 +528,7 @@ def main():
                 print("oracle: " + json.dumps(rec), flush=True)
         return
     if args.summarize:
-        pmc = "rocprofv3 {opts} -- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-mib 256"
+        pmc = "rocprofv3 {opts} -- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-clock --copy-mib 256"
         summarize(*args.summarize, copy_mib=256,
                   cmds={"fetch": pmc.format(opts="--pmc FETCH_SIZE --output-format csv"),
                         "write": pmc.format(opts="--pmc WRITE_SIZE --output-format csv"),
@@ -520,7 +593,10 @@ def main():
                                 "f32": "fwd_f32_kernel", "fp8": "fwd_fp8_kernel"}[w.dtype],
                      "launch_ms_mean": round(mean_ms, 5), "launch_ms_median": round(med_ms, 5),
                      "launch_ms_min": round(min_ms, 5),
-                     "algorithmic_bytes": algorithmic_bytes(w)},
+                     "algorithmic_bytes": algorithmic_bytes(w),
+                     "hbm_gbs": round(algorithmic_bytes(w) / (mean_ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(algorithmic_bytes(w) / (mean_ms * 1e-3) / 1e9
+                                       / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
         # The same shape's backward (prep, dK/dV and dQ kernels), counted as
         # 2.5x the forward's FLOPs (five N x N x D products against two).
@@ -529,6 +605,13 @@ def main():
             "frac_of_mfma_peak": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),
             "flops": 2.5 * flops},
     }
+    if not args.no_clock and w.dtype in ("bf16", "f16"):
+        clk = sample_gfx_clock(fwd)
+        if clk.get("mhz"):
+            peak_clk = MI355X_CUS * BF16_FLOP_PER_CLK_PER_CU * clk["mhz"] * 1e6 / 1e12
+            clk["peak_tflops_at_clock"] = round(peak_clk, 1)
+            clk["frac_at_clock"] = round(kernel_tflops / peak_clk, 4)
+        line["clock"] = clk
     if args.extra:
         for name, wk in WORKLOADS.items():
             tf, tb, _ = run_workload(wk, 20, 3, backward=wk.backward or name == METRIC_WORKLOAD)

@@ -323,10 +323,6 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
   }
 
   // Lane holds dK^T / dV^T rows (d) 32 d + 8 g + 4 hf + (0..3) of its key.
-#pragma unroll
-  for (int d = 0; d < C::DB; ++d) {
-
-  }
   if (key < N) {
     T* dkrow = (T*)p.dk + gbase + (size_t)key * p.rs_g;
     T* dvrow = (T*)p.dv + gbase + (size_t)key * p.rs_g;
