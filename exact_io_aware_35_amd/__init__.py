@@ -8,5 +8,6 @@ from .binding import (  # noqa: F401
     FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FaError, PreparedCall, backward, backward_qkvpacked, forward,
     forward_fp8, forward_qkvpacked, load_library, prepare_forward, prepare_forward_fp8,
     workspace_size,
+    backward_noalloc,
 )
 from .autograd import FlashAttention, flash_attention  # noqa: F401

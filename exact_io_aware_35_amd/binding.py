@@ -41,6 +41,8 @@ SIGNATURES = [
                             _F, _I, _I, _I, _I, _P, _SZ, _P]),
     ("fa_forward_fp8", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _F, _I, _I, _I,
                             _P]),
+    ("fa_backward_noalloc", _I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I,
+                                 _I, _I, _I, _P]),
     ("fa_status_string", ctypes.c_char_p, [_I]),
     ("fa_last_error_message", ctypes.c_char_p, []),
 ]
@@ -351,3 +353,32 @@ def backward_qkvpacked(qkv, out, lse, dout, causal=False, window=(-1, -1), softm
     _backward(qkv, None, None, True, (B, N, H, D), out, lse, dout, causal, window,
               softmax_scale, seqlens_k, alibi_slopes, (dqkv, None, None), workspace, stream)
     return dqkv
+
+
+def backward_noalloc(q, k, v, out, lse, dout, causal=False, window=(-1, -1), softmax_scale=None,
+                     seqlens_k=None, dq=None, dk=None, dv=None, stream=None):
+    """backward() through fa_backward_noalloc: the library's static scratch
+    array stands in for the workspace (no device allocation inside the call;
+    the output tensors are allocated here unless given)."""
+    import torch
+    shape = tuple(q.shape)
+    _check_forward_buffers(q, k, v, shape, out, lse, seqlens_k, (q.dtype,))
+    if out is None or lse is None or dout is None:
+        raise FaError(FA_ERR_INVALID_ARG, "out, lse and dout are required")
+    _expect(dout, "dout", shape, (q.dtype,), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name in zip((dq, dk, dv), ("dq", "dk", "dv")):
+        _expect(t, name, shape, (q.dtype,), q.device)
+    lib = load_library()
+    B, N, H, D = shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    st = lib.fa_backward_noalloc(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                 _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                                 _dev_ptr(dout, "dout"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
+                                 _dev_ptr(dv, "dv"), _dev_ptr(seqlens_k, "seqlens_k"), B, H, N, D,
+                                 scale, int(bool(causal)), int(window[0]), int(window[1]),
+                                 _dtype_code(q), _stream_handle(stream, q.device))
+    _check(lib, st)
+    return dq, dk, dv

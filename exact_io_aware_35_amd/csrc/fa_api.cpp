@@ -140,6 +140,18 @@ BwdWorkspace bwd_workspace(int batch, int heads, int seqlen, int headdim) {
 
 }  // namespace
 
+namespace fa {
+
+fa_status_t report(fa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 const char* fa_status_string(fa_status_t s) {

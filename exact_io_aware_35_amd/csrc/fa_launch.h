@@ -3,9 +3,14 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "fa.h"
 #include "fa_params.h"
 
 namespace fa {
+
+// Record the detail fa_last_error_message() returns for status s on this
+// thread (printf-style); returns s.
+fa_status_t report(fa_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // Element type of Q, K, V, O (and dO and the gradients in the backward).
 enum class ElemType { kBF16, kF32, kF16 };

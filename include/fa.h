@@ -230,6 +230,35 @@ fa_status_t fa_forward_fp8(const void* q, const void* k, const void* v,
                            float descale_v, int causal,
                            int window_left, int window_right, hipStream_t stream);
 
+/*
+ * fa_backward_noalloc -- fa_backward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. The workspace is not a caller buffer but a static
+ * device array inside the library of FA_NOALLOC_SCRATCH_BYTES bytes; each GPU
+ * the library runs on holds its own copy from the library's load until the
+ * process ends. The call allocates nothing (no hipMalloc or hipFree, no
+ * allocating library routine); it looks the array's address up once per
+ * device, on its first call with that device current.
+ * Arguments, results, conventions and errors are those of fa_backward without
+ * the workspace arguments. Sizes whose fa_backward_workspace_size exceeds
+ * FA_NOALLOC_SCRATCH_BYTES return FA_ERR_WORKSPACE before anything is read or
+ * launched (128 MiB serves, for instance, batch 2, 8 heads, seqlen 4096,
+ * headdim 128). Whatever the backward needs cleared, its kernels clear on the
+ * device; the array keeps the last call's contents.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (on different streams, or from several host threads) race and give
+ * undefined results. Serialise them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+fa_status_t fa_backward_noalloc(const void* q, const void* k, const void* v,
+                                const void* out, const float* lse, const void* dout,
+                                void* dq, void* dk, void* dv,
+                                const int32_t* seqlens_k,
+                                int batch, int heads, int seqlen, int headdim,
+                                float softmax_scale, int causal,
+                                int window_left, int window_right,
+                                fa_dtype_t dtype, hipStream_t stream);
+
 /* Static English name of a status code. Never NULL. */
 const char* fa_status_string(fa_status_t status);
 

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_backward", "fa_forward_ex", "fa_backward_ex", "fa_forward_fp8",
-         "fa_backward_workspace_size", "fa_status_string", "fa_last_error_message"])
+         "fa_backward_workspace_size", "fa_backward_noalloc", "fa_status_string",
+         "fa_last_error_message"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -243,3 +244,24 @@ def test_fp8_binding_rejects_other_byte_types():
     x = torch.zeros((1, 4, 1, 64), dtype=torch.float8_e5m2)
     with pytest.raises(fb.FaError, match="e4m3"):
         fb.forward_fp8(x, x, x)
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """fa_backward_noalloc refuses sizes whose workspace exceeds the static
+    scratch before it reads a pointer or touches the GPU; an empty call is
+    accepted and does nothing."""
+    lib = fb.load_library()
+    limit = 128 << 20
+    B, H, N, D = 64, 16, 4096, 128
+    assert lib.fa_backward_workspace_size(B, H, N, D, fb.FA_DTYPE_BF16) > limit
+    st = lib.fa_backward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 B, H, N, D, 0.1, 0, -1, -1, fb.FA_DTYPE_BF16, None)
+    assert st == fb.FA_ERR_WORKSPACE
+    msg = lib.fa_last_error_message().decode()
+    assert "no-alloc scratch holds 134217728" in msg, msg
+    st = lib.fa_backward_noalloc(None, None, None, None, None, None, None, None, None, None,
+                                 0, H, N, D, 0.1, 0, -1, -1, fb.FA_DTYPE_BF16, None)
+    assert st == fb.FA_OK
+    st = lib.fa_backward_noalloc(None, None, None, None, None, None, None, None, None, None,
+                                 1, 1, 16, 96, 0.1, 0, -1, -1, fb.FA_DTYPE_BF16, None)
+    assert st == fb.FA_ERR_UNSUPPORTED
