@@ -121,10 +121,12 @@ fa_status_t check_alibi(const float* slopes, int bstride, int heads) {
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Backward workspace: the row statistics (2 floats per row), then fp16
-// copies of Q, K and dO; each part starts on a 256-byte boundary.
+// Backward workspace: the row statistics (2 floats per row), fp16 copies
+// of Q, K and dO, then the pre-pass's per-block maxima of |Q|, |K|, |V|,
+// |dO| (kMaxParts blocks of 4 floats per (batch, head)); each part starts
+// on a 256-byte boundary.
 struct BwdWorkspace {
-  size_t stats, q16, k16, do16, total;
+  size_t stats, q16, k16, do16, part, total;
 };
 BwdWorkspace bwd_workspace(int batch, int heads, int seqlen, int headdim) {
   const size_t rows = (size_t)batch * heads * seqlen;
@@ -134,7 +136,8 @@ BwdWorkspace bwd_workspace(int batch, int heads, int seqlen, int headdim) {
   w.q16 = round256(rows * 2 * sizeof(float));
   w.k16 = w.q16 + half;
   w.do16 = w.k16 + half;
-  w.total = w.do16 + half;
+  w.part = w.do16 + half;
+  w.total = w.part + (rows == 0 ? 0 : round256((size_t)batch * heads * fa::kMaxParts * 4 * sizeof(float)));
   return w;
 }
 
@@ -335,6 +338,7 @@ fa_status_t fa_backward_ex(const void* q, const void* k, const void* v, int qkv_
   p.q16 = wsb + ws.q16;
   p.k16 = wsb + ws.k16;
   p.do16 = wsb + ws.do16;
+  p.part = reinterpret_cast<float*>(wsb + ws.part);
   p.mask.seqlens_k = seqlens_k;
   p.mask.wl = wl;
   p.mask.wr = wr;

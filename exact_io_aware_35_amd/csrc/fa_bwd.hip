@@ -11,10 +11,14 @@
 // (The article's code sums P * dP over one key block only; the full-row sum
 // is what its own Jacobian gives, and is what is used here.)
 //
-// Three kernels, no atomics, so the result is deterministic (the flash_attn
+// Four kernels, no atomics, so the result is deterministic (the flash_attn
 // docstring's deterministic backward, claire-chang.com notes):
 //   bwd_prep_kernel : per row D_i (from O and dO) and LSE log2 e; fp16 copies
-//                     of Q, K and dO (bandwidth-bound, one pass).
+//                     of Q, K and dO; per block the maxima of |Q|, |K|, |V|,
+//                     |dO| (bandwidth-bound, one pass).
+//   bwd_rescale_kernel : rewrites the copies of a slice whose maxima leave
+//                     fp16's comfortable range (operand range, below);
+//                     returns at once for every other slice.
 //   bwd_dkdv_kernel : one work-group per key block; each wave keeps K, V, dK
 //                     and dV of 32 keys in registers and streams the query
 //                     tiles (Q, dO and the row statistics) through LDS.
@@ -39,44 +43,152 @@ namespace fa {
 
 // ---------------------------------------------------------------- pre-pass
 
-// One 16-byte chunk of one (b, i, h) row per thread: D_i = sum_d dO O (fp32),
-// the fp16 copies of the Q, K and dO chunks, and per row the statistics pair
-// (LSE log2 e, or +inf for a row with no visible key; D_i).
+// Operand range. The products with P or dS take fp16 operands, so Q, K and dO
+// are copied to fp16 and V is converted in registers. Each of the four is
+// used as it is when its largest magnitude in the (b, h) slice lies in
+// [2^-6, 8]: every value then converts without overflow, values down to 2^-8
+// of the largest stay normal, and |dS| <= |dP| + |D| <= 2 headdim max|dO|
+// max|V| <= 2^15 fits fp16. A slice whose maximum lies outside that range
+// (bf16 values above fp16's 65504, gradients of 1e-6, ...) is scaled by an
+// exact power of two 2^e that brings the maximum into [4, 8) (|e| <= 40); the
+// kernels fold e into the exponent's scale and the epilogues, where each
+// power of two is exact, so the result is that of the scaled slice up to the
+// same fp16 roundings (l189.com from-scratch article §5.2: keep every
+// intermediate inside the format's range).
+constexpr float kRangeLo = 0x1p-6f, kRangeHi = 8.f;
+
+__device__ __forceinline__ int range_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.4e38f) || (m >= kRangeLo && m <= kRangeHi)) return 0;
+  int ex;
+  (void)frexpf(m, &ex);  // m = f 2^ex, f in [0.5, 1)
+  return min(40, max(-40, 3 - ex));
+}
+
+// Exponents (Q, K, dO, V) of slice bh from the pre-pass's block maxima
+// (wave-uniform; every lane of the calling wave takes part).
+struct SliceExp {
+  int q, k, o, v;
+};
+__device__ __forceinline__ SliceExp slice_exp(const BwdParams& p, int bh) {
+  const int lane = threadIdx.x & 63;
+  f32x4_t m = f32x4_t{};
+  if (lane < p.np) m = ld_global<f32x4_t>(p.part + ((size_t)bh * kMaxParts + lane) * 4);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m[t] = fmaxf(m[t], __shfl_xor(m[t], sh, 64));
+  SliceExp e;
+  e.q = __builtin_amdgcn_readfirstlane(range_exp(m[0]));
+  e.k = __builtin_amdgcn_readfirstlane(range_exp(m[1]));
+  e.v = __builtin_amdgcn_readfirstlane(range_exp(m[2]));
+  e.o = __builtin_amdgcn_readfirstlane(range_exp(m[3]));
+  return e;
+}
+
+// 8 values of type T -> 8 fp16 values of x 2^e, rounded to nearest even.
+template <typename T>
+__device__ __forceinline__ u32x4_t to_f16x8_scaled(u32x4_t u, int e) {
+  using E = Elt16<T>;
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = pack_f16x2(ldexpf(E::lo(u[j]), e), ldexpf(E::hi(u[j]), e));
+  return r;
+}
+
+// One work-group per (b, h) and block of p.prows rows; one 16-byte chunk of
+// one row per thread per pass: D_i = sum_d dO O (fp32), the fp16 copies of
+// the Q, K and dO chunks, per row the statistics pair (LSE log2 e, or +inf for
+// a row with no visible key; D_i), and per block the maxima of |Q|, |K|, |V|,
+// |dO| (NaN inputs do not raise them).
 template <int D, typename T>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   using E = Elt16<T>;
   constexpr int LPR = D / 8;               // lanes per row, 16 bytes each
-  constexpr int RPB = 256 / LPR;           // rows per block
-  const int tid = threadIdx.x;
-  const long long r = (long long)blockIdx.x * RPB + tid / LPR;  // flattened (b, i, h)
-  const int c = tid % LPR;
-  const long long R = (long long)p.B * p.N * p.H;
-  float acc = 0.f;
-  if (r < R) {
-    const long long bi = r / p.H;                 // b * N + i
-    const size_t hd = (size_t)(r - bi * p.H) * D + 8 * c;
-    const size_t e = (size_t)r * D + 8 * c;       // the fp16 copies are [B][N][H][D]
-    const size_t eq = (size_t)bi * p.rs_q + hd, eo = (size_t)bi * p.rs_o + hd;
-    const u32x4_t o = ld_global<u32x4_t>((const T*)p.o + eo);
-    const u32x4_t g = ld_global<u32x4_t>((const T*)p.dout + eo);
-    const u32x4_t q = ld_global<u32x4_t>((const T*)p.q + eq);
-    const u32x4_t k = ld_global<u32x4_t>((const T*)p.k + eq);
+  constexpr int RPB = 256 / LPR;           // rows per pass
+  __shared__ f32x4_t red[4];
+  const int tid = threadIdx.x, c = tid % LPR;
+  const int bh = blockIdx.x / p.np, pb = blockIdx.x - bh * p.np;
+  const int b = bh / p.H, h = bh - b * p.H;
+  f32x4_t mx = f32x4_t{};
+  // p.prows is a multiple of RPB: every thread runs the same passes (the
+  // row sum below is a shuffle over the LPR lanes of a row).
+  for (int pass = 0; pass < p.prows / RPB; ++pass) {
+    const int i = pb * p.prows + pass * RPB + tid / LPR;
+    float acc = 0.f;
+    const bool live = i < p.N;
+    if (live) {
+      const size_t bi = (size_t)b * p.N + i;
+      const size_t hd = (size_t)h * D + 8 * c;
+      const size_t e = (bi * p.H) * D + hd;        // the fp16 copies are [B][N][H][D]
+      const size_t eq = bi * p.rs_q + hd, eo = bi * p.rs_o + hd;
+      const u32x4_t o = ld_global<u32x4_t>((const T*)p.o + eo);
+      const u32x4_t g = ld_global<u32x4_t>((const T*)p.dout + eo);
+      const u32x4_t q = ld_global<u32x4_t>((const T*)p.q + eq);
+      const u32x4_t k = ld_global<u32x4_t>((const T*)p.k + eq);
+      const u32x4_t v = ld_global<u32x4_t>((const T*)p.v + eq);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc += E::lo(o[j]) * E::lo(g[j]) + E::hi(o[j]) * E::hi(g[j]);
-    *(u32x4_t*)((_Float16*)p.do16 + e) = E::to_f16x8(g);
-    *(u32x4_t*)((_Float16*)p.q16 + e) = E::to_f16x8(q);
-    *(u32x4_t*)((_Float16*)p.k16 + e) = E::to_f16x8(k);
+      for (int j = 0; j < 4; ++j) {
+        acc += E::lo(o[j]) * E::lo(g[j]) + E::hi(o[j]) * E::hi(g[j]);
+        mx[0] = fmaxf(mx[0], fmaxf(fabsf(E::lo(q[j])), fabsf(E::hi(q[j]))));
+        mx[1] = fmaxf(mx[1], fmaxf(fabsf(E::lo(k[j])), fabsf(E::hi(k[j]))));
+        mx[2] = fmaxf(mx[2], fmaxf(fabsf(E::lo(v[j])), fabsf(E::hi(v[j]))));
+        mx[3] = fmaxf(mx[3], fmaxf(fabsf(E::lo(g[j])), fabsf(E::hi(g[j]))));
+      }
+      *(u32x4_t*)((_Float16*)p.do16 + e) = E::to_f16x8(g);
+      *(u32x4_t*)((_Float16*)p.q16 + e) = E::to_f16x8(q);
+      *(u32x4_t*)((_Float16*)p.k16 + e) = E::to_f16x8(k);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (live && c == 0) {
+      const size_t s = (size_t)bh * p.N + i;
+      const float L = p.lse[s];
+      *(f32x2_t*)(p.stats + 2 * s) = f32x2_t{L == -INFINITY ? INFINITY : L * 1.4426950408889634f, acc};
+    }
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (r < R && c == 0) {
-    const int h = (int)(r % p.H);
-    const long long bi = r / p.H;
-    const int i = (int)(bi % p.N), b = (int)(bi / p.N);
-    const size_t s = ((size_t)b * p.H + h) * p.N + i;
-    const float L = p.lse[s];
-    *(f32x2_t*)(p.stats + 2 * s) = f32x2_t{L == -INFINITY ? INFINITY : L * 1.4426950408889634f, acc};
+  for (int sh = 32; sh >= 1; sh >>= 1)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], sh, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    f32x4_t r = red[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r[t] = fmaxf(r[t], red[w][t]);
+    *(f32x4_t*)(p.part + ((size_t)bh * kMaxParts + pb) * 4) = r;
+  }
+}
+
+// Rewrites the fp16 copies of a slice that needs a power-of-two scale
+// (range_exp above) and scales its D_i by 2^(e_dO + e_V), the factor dP
+// carries in the dK/dV pass. kRescaleGroups work-groups per (b, h); one whose
+// slice needs no scale returns at once (the common case costs one small
+// launch).
+constexpr int kRescaleGroups = 4;
+template <int D, typename T>
+__global__ void __launch_bounds__(256) bwd_rescale_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x, c = tid % LPR;
+  const int bh = blockIdx.x / kRescaleGroups, g = blockIdx.x - bh * kRescaleGroups;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const SliceExp ex = slice_exp(p, bh);
+  if ((ex.q | ex.k | ex.o | ex.v) == 0) return;
+  for (int i = g * RPB + tid / LPR; i < p.N; i += kRescaleGroups * RPB) {
+    const size_t bi = (size_t)b * p.N + i;
+    const size_t hd = (size_t)h * D + 8 * c;
+    const size_t e = (bi * p.H) * D + hd;
+    const size_t eq = bi * p.rs_q + hd, eo = bi * p.rs_o + hd;
+    if (ex.o) *(u32x4_t*)((_Float16*)p.do16 + e) = to_f16x8_scaled<T>(ld_global<u32x4_t>((const T*)p.dout + eo), ex.o);
+    if (ex.q) *(u32x4_t*)((_Float16*)p.q16 + e) = to_f16x8_scaled<T>(ld_global<u32x4_t>((const T*)p.q + eq), ex.q);
+    if (ex.k) *(u32x4_t*)((_Float16*)p.k16 + e) = to_f16x8_scaled<T>(ld_global<u32x4_t>((const T*)p.k + eq), ex.k);
+    if (c == 0 && (ex.o + ex.v) != 0) {
+      float* d = p.stats + 2 * ((size_t)bh * p.N + i) + 1;
+      *d = ldexpf(*d, ex.o + ex.v);
+    }
   }
 }
 
@@ -126,6 +238,11 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
   const size_t gbase = (size_t)b * N * p.rs_g + (size_t)h * D;
   float slope2 = 0.f;  // ALiBi slope in the log2 domain of the exponent
   if constexpr (ALIBI) slope2 = alibi_raw_slope(p.alibi, b, h, p.scale_log2) * p.scale_log2;
+  // Operand exponents of the slice: scores of the fp16 copies carry
+  // 2^(e_Q + e_K), dP carries 2^(e_dO + e_V) (as does D_i after the rescale
+  // pass), dV^T 2^e_dO and dK^T 2^(e_Q + e_dO + e_V).
+  const SliceExp ex = slice_exp(p, bh);
+  const float sl2 = ldexpf(p.scale_log2, -(ex.q + ex.k));
 
   // This lane's key, and its K and V rows as fp16 B operands:
   // kf[s] = K[key][16 s + 8 hf .. +8). Keys past N are clamped (and masked).
@@ -139,7 +256,7 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       kf[s] = ld_global<f16x8_t>((const _Float16*)p.k16 + off + 16 * s);
-      vf[s] = __builtin_bit_cast(f16x8_t, E::to_f16x8(ld_global<u32x4_t>((const T*)p.v + voff + 16 * s)));
+      vf[s] = __builtin_bit_cast(f16x8_t, to_f16x8_scaled<T>(ld_global<u32x4_t>((const T*)p.v + voff + 16 * s), ex.v));
     }
   }
 
@@ -255,8 +372,8 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const f32x4_t r = st2[i >> 1];  // rows of elements i and i + 1: (L2, D, L2, D)
-        float x0 = fmaf(sa[i], p.scale_log2, -r[0]);
-        float x1 = fmaf(sa[i + 1], p.scale_log2, -r[2]);
+        float x0 = fmaf(sa[i], sl2, -r[0]);
+        float x1 = fmaf(sa[i + 1], sl2, -r[2]);
         if constexpr (ALIBI) {
           x0 = fmaf(fabsf(di + (float)(8 * (i >> 2) + (i & 3))), -slope2, x0);
           x1 = fmaf(fabsf(di + (float)(8 * (i >> 2) + (i & 3) + 1)), -slope2, x1);
@@ -326,16 +443,19 @@ __global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p
   if (key < N) {
     T* dkrow = (T*)p.dk + gbase + (size_t)key * p.rs_g;
     T* dvrow = (T*)p.dv + gbase + (size_t)key * p.rs_g;
+    const int xk = -(ex.q + ex.o + ex.v), xv = -ex.o;
+    auto gk = [&](float a) { return ldexpf(a * p.scale, xk); };
+    auto gv = [&](float a) { return ldexpf(a, xv); };
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
         *(u32x2_t*)(dkrow + col) =
-            u32x2_t{E::pack2(dk[d][4 * g] * p.scale, dk[d][4 * g + 1] * p.scale),
-                    E::pack2(dk[d][4 * g + 2] * p.scale, dk[d][4 * g + 3] * p.scale)};
-        *(u32x2_t*)(dvrow + col) = u32x2_t{E::pack2(dv[d][4 * g], dv[d][4 * g + 1]),
-                                           E::pack2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
+            u32x2_t{E::pack2(gk(dk[d][4 * g]), gk(dk[d][4 * g + 1])),
+                    E::pack2(gk(dk[d][4 * g + 2]), gk(dk[d][4 * g + 3]))};
+        *(u32x2_t*)(dvrow + col) = u32x2_t{E::pack2(gv(dv[d][4 * g]), gv(dv[d][4 * g + 1])),
+                                           E::pack2(gv(dv[d][4 * g + 2]), gv(dv[d][4 * g + 3]))};
       }
   }
 }
@@ -398,8 +518,11 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
   const size_t base = ((size_t)b * N * p.H + h) * D;
   const size_t vbase = (size_t)b * N * p.rs_q + (size_t)h * D;
   const size_t gbase = (size_t)b * N * p.rs_g + (size_t)h * D;
-  float slope_raw = 0.f;
-  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
+  // Operand exponents of the slice (see the one-wave form).
+  const SliceExp ex = slice_exp(p, bh);
+  const float sl2 = ldexpf(p.scale_log2, -(ex.q + ex.k));
+  float slope_raw = 0.f;  // in the units of the scaled scores
+  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, sl2);
 
   // This lane's key; the wave's B operand is its K row (role 0) or V row
   // (role 1) in fp16. Keys past N are clamped (and masked).
@@ -416,7 +539,7 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
       const size_t off = vbase + (size_t)kr * p.rs_q + 8 * hf;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s)
-        kv[s] = __builtin_bit_cast(f16x8_t, E::to_f16x8(ld_global<u32x4_t>((const T*)p.v + off + 16 * s)));
+        kv[s] = __builtin_bit_cast(f16x8_t, to_f16x8_scaled<T>(ld_global<u32x4_t>((const T*)p.v + off + 16 * s), ex.v));
     }
   }
 
@@ -526,8 +649,8 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
           }
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
-            const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -l4[i >> 2][(i & 3) + 1]));
+            const float p0 = exp2_fast(fmaf(sa[i], sl2, -l4[i >> 2][i & 3]));
+            const float p1 = exp2_fast(fmaf(sa[i + 1], sl2, -l4[i >> 2][(i & 3) + 1]));
             pk[2 * qs + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0, p1);
           }
         }
@@ -632,6 +755,8 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
   // of its key.
   if (key < N) {
     const float sc = role == 0 ? 1.f : p.scale;
+    const int xs = role == 0 ? -ex.o : -(ex.q + ex.o + ex.v);
+    auto gs = [&](float a) { return ldexpf(a * sc, xs); };
     T* row = (T*)(role == 0 ? p.dv : p.dk) + gbase + (size_t)key * p.rs_g;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
@@ -639,8 +764,8 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
         *(u32x2_t*)(row + col) =
-            u32x2_t{E::pack2(acc[d][4 * g] * sc, acc[d][4 * g + 1] * sc),
-                    E::pack2(acc[d][4 * g + 2] * sc, acc[d][4 * g + 3] * sc)};
+            u32x2_t{E::pack2(gs(acc[d][4 * g]), gs(acc[d][4 * g + 1])),
+                    E::pack2(gs(acc[d][4 * g + 2]), gs(acc[d][4 * g + 3]))};
       }
   }
 }
@@ -687,8 +812,14 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   const size_t obase = (size_t)b * N * p.rs_o + (size_t)h * D;
   const size_t vbase = (size_t)b * N * p.rs_q + (size_t)h * D;
   const size_t gbase = (size_t)b * N * p.rs_g + (size_t)h * D;
-  float slope_raw = 0.f;
-  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, p.scale_log2);
+  // Operand exponents of the slice: S from the fp16 copies carries
+  // 2^(e_Q + e_K); dP comes from the raw V and dO, and dS is formed as
+  // P 2^(e_dO + e_V) (dP - D), the scale dK/dV's dS has (and within fp16's
+  // range); dQ^T = K^T dS^T then carries 2^(e_K + e_dO + e_V).
+  const SliceExp ex = slice_exp(p, bh);
+  const float sl2 = ldexpf(p.scale_log2, -(ex.q + ex.k));
+  float slope_raw = 0.f;  // in the units of the scaled scores
+  if constexpr (ALIBI) slope_raw = alibi_raw_slope(p.alibi, b, h, sl2);
 
   const int q0 = qblk * C::BM, wq0 = q0 + wave * 32;
   int klo, khi;
@@ -712,7 +843,11 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
     }
   }
   const f32x2_t st = ld_global<f32x2_t>(p.stats + 2 * (((size_t)b * p.H + h) * N + qrow));
+  // D_i arrives scaled by 2^(e_dO + e_V) (the rescale pass); dS takes the
+  // same factor as fma(dP, 2^(e_dO + e_V), -D_i): the power of two is exact,
+  // so the scaled dS is the unscaled one times that power.
   const float lse2 = qi >= N ? INFINITY : st[0], dr = st[1];
+  const float spv = ldexpf(1.f, ex.o + ex.v);
 
   // K (fp16 copy) and V (input) rows sit rs and rs_q elements apart.
   const int krs2 = rs * 2, vrs2 = p.rs_q * 2;
@@ -785,9 +920,10 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
       }
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = exp2_fast(fmaf(sa[i], p.scale_log2, -lse2));
-        const float p1 = exp2_fast(fmaf(sa[i + 1], p.scale_log2, -lse2));
-        dsk[2 * kb + (i >> 3)][(i & 7) >> 1] = pack_f16x2(p0 * (pa[i] - dr), p1 * (pa[i + 1] - dr));
+        const float p0 = exp2_fast(fmaf(sa[i], sl2, -lse2));
+        const float p1 = exp2_fast(fmaf(sa[i + 1], sl2, -lse2));
+        dsk[2 * kb + (i >> 3)][(i & 7) >> 1] =
+            pack_f16x2(p0 * fmaf(pa[i], spv, -dr), p1 * fmaf(pa[i + 1], spv, -dr));
       }
     }
 #pragma unroll
@@ -821,14 +957,16 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
 
   if (qi < N) {
     T* row = (T*)p.dq + gbase + (size_t)qi * p.rs_g;
+    const int xq = -(ex.k + ex.o + ex.v);
+    auto gq = [&](float a) { return ldexpf(a * p.scale, xq); };
 #pragma unroll
     for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * d + 8 * g + 4 * hf;
         *(u32x2_t*)(row + col) =
-            u32x2_t{E::pack2(dq[d][4 * g] * p.scale, dq[d][4 * g + 1] * p.scale),
-                    E::pack2(dq[d][4 * g + 2] * p.scale, dq[d][4 * g + 3] * p.scale)};
+            u32x2_t{E::pack2(gq(dq[d][4 * g]), gq(dq[d][4 * g + 1])),
+                    E::pack2(gq(dq[d][4 * g + 2]), gq(dq[d][4 * g + 3]))};
       }
   }
 }
@@ -837,10 +975,16 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
 
 template <int D, bool ALIBI, typename T>
 static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.N * p.H;
-  const long long rpb = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<D, T>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
-                     stream, p);
+  // Pre-pass blocks: at most kMaxParts per (b, h), each a whole number of
+  // 256-thread passes (256 / (D / 8) rows each).
+  constexpr int rpb = 256 / (D / 8);
+  const int passes = (p.N + kMaxParts * rpb - 1) / (kMaxParts * rpb);
+  p.prows = passes * rpb;
+  p.np = (p.N + p.prows - 1) / p.prows;
+  const dim3 pgrid((unsigned)((long long)p.B * p.H * p.np));
+  hipLaunchKernelGGL((bwd_prep_kernel<D, T>), pgrid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_rescale_kernel<D, T>), dim3((unsigned)((long long)p.B * p.H * kRescaleGroups)),
+                     dim3(256), 0, stream, p);
   // Measured on MI355X: the one-wave form is faster at headdim 64 (two
   // waves per SIMD either way, half the barriers); at headdim 128 only the
   // pair form keeps its state in VGPRs.

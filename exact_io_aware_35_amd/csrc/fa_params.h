@@ -39,6 +39,10 @@ struct FwdParams {
   int longest_first;     // 1: dispatch the query blocks with most keys first
 };
 
+// Blocks of rows per (batch, head) whose maxima the backward's pre-pass
+// records; every backward kernel reduces them to the (b, h) maxima.
+constexpr int kMaxParts = 64;
+
 struct BwdParams {
   const void* q;
   const void* k;
@@ -55,6 +59,10 @@ struct BwdParams {
   void* q16;             // Q, K and dO in fp16, [B][N][H][D] like the inputs
   void* k16;
   void* do16;
+  float* part;           // per (b, h) and block of prows rows: max |Q|, |K|, |V|, |dO|,
+                         // [B * H][np][4]
+  int np;                // blocks of rows per (b, h) in the pre-pass (<= kMaxParts)
+  int prows;             // rows per such block
   MaskParams mask;
   AlibiParams alibi;
   int B, H, N;

@@ -103,8 +103,9 @@ fa_status_t fa_forward(const void* q, const void* k, const void* v,
  * fa_backward_workspace_size -- bytes of device workspace fa_backward needs
  * for these sizes: per row the fp32 pair (LSE log2 e, D_i = sum_d dO_id O_id),
  * [batch][heads][seqlen][2], then fp16 copies of Q, K and dO (each
- * batch*seqlen*heads*headdim*2 bytes), every part rounded up to 256 bytes.
- * Returns 0 for invalid sizes.
+ * batch*seqlen*heads*headdim*2 bytes), then per (batch, head) 64 groups of
+ * 4 fp32 maxima (|Q|, |K|, |V|, |dO| over blocks of rows), every part rounded
+ * up to 256 bytes. Returns 0 for invalid sizes and for empty calls.
  */
 size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
                                   fa_dtype_t dtype);
@@ -129,8 +130,16 @@ size_t fa_backward_workspace_size(int batch, int heads, int seqlen, int headdim,
  * dtype is FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32 returns
  * FA_ERR_UNSUPPORTED).
  * Precision: every product with P or dS as an operand takes fp16 operands
- * (bf16 Q, K and dO are converted, exactly for magnitudes in fp16's normal
- * range); Q, K and dO must lie below 65504 in magnitude.
+ * (fp32 accumulation), and so do the products that recompute S and dP from
+ * those copies. Within each (batch, head) slice, Q, K, V and dO are used as
+ * they are when their largest magnitude lies in [2^-6, 8]; a tensor whose
+ * slice maximum lies outside it is scaled by an exact power of two 2^e,
+ * |e| <= 40, that brings the maximum into [4, 8), and the kernels undo the
+ * scale exactly ([scratch] §5.2, numerical stability). Any finite input
+ * whose slice maxima lie within [2^-38, 2^42] is therefore handled with the
+ * same relative precision: no fp16 overflow, and no loss to fp16's
+ * subnormal range above 2^-8 of the slice maximum. The gradients must be
+ * finite in the output dtype.
  */
 fa_status_t fa_backward(const void* q, const void* k, const void* v,
                         const void* out, const float* lse, const void* dout,

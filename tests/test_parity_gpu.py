@@ -538,3 +538,78 @@ def test_alibi_workload_b2h8n4096d128_sampled_rows():
             r = rows[h]
             assert_close(o[b, r, h, :], ro[b, h], TOL["bf16"]["o"], f"O[b={b},h={h}]")
             assert_lse(lse[b, h, r].numpy().astype(np.float64), rl[b, h], TOL["bf16"]["lse"])
+
+
+# ---------------------------------------------------------------- operand range of the backward
+
+RANGE_CASES = {
+    # dtype: exponents (Q, K, V, dO) applied to a standard case. bf16: Q and V
+    # far above fp16's 65504, K and dO far below its normal range (gradients
+    # around 1e-7). fp16: V and dO large enough that dP = dO V^T, unscaled,
+    # would leave fp16's range in dS.
+    "bf16": (20, -20, 17, -24),
+    "f16": (0, 0, 6, 6),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("alibi", [False, True], ids=["plain", "alibi"])
+def test_backward_operand_range(dtype, D, alibi):
+    """Inputs that are exact power-of-two multiples of a standard case,
+    Q 2^a, K 2^b, V 2^c, dO 2^d, give exactly the standard case's results
+    times the matching powers: O 2^c and the same LSE; dV 2^d, dK 2^(a+c+d),
+    dQ 2^(b+c+d) (S is unchanged, dP, D and dS carry 2^(c+d)). The backward
+    rescales each slice's fp16 operand copies by a power of two when its
+    maximum leaves [2^-6, 8] (into [4, 8)), so with the standard slices'
+    maxima in [4, 8) the scaled case runs on the same fp16 operands and must
+    match bitwise; both also match the oracle, with the tolerance scaled like
+    the result ([scratch] §5.2, keeping intermediates inside the format's
+    range)."""
+    ea, eb, ec, ed = RANGE_CASES[dtype]
+    d = make_case(2, 300, 3, D, dtype=dtype, seed=51, backward=True, seqlens_k=[300, 211])
+    # Bring each (b, h) slice's largest magnitude into [4, 8) by a power of
+    # two (exact), where the scaled case's copies land too: both cases then
+    # run on the same fp16 operands (fp16 subnormals would not scale exactly).
+    for x in ("q", "k", "v", "dout"):
+        t = d[x].double()
+        m = t.abs().amax(dim=(1, 3), keepdim=True)
+        d[x] = (t * torch.exp2(2.0 - torch.floor(torch.log2(m)))).to(d[x].dtype)
+        m = d[x].double().abs().amax(dim=(1, 3))
+        assert ((m >= 4) & (m < 8)).all()
+    mask = dict(causal=True)
+    sl = dev(geometric_slopes(3)) if alibi else None
+    tdt = d["q"].dtype
+    sc = lambda t, e: (t.double() * 2.0 ** e).to(tdt)
+    std = [dev(d[x]) for x in ("q", "k", "v", "dout")]
+    big = [dev(sc(d[x], e)) for x, e in zip(("q", "k", "v", "dout"), (ea, eb, ec, ed))]
+    for t, s_, e in zip(big, std, (ea, eb, ec, ed)):  # the scaling itself is exact
+        assert torch.equal(t.double(), s_.double() * 2.0 ** e)
+    sk = dev(d["seqlens_k"])
+    runs = []
+    for q, k, v, do in (std, big):
+        o, lse = forward(q, k, v, seqlens_k=sk, alibi_slopes=sl, **mask)
+        g = backward(q, k, v, o, lse, do, seqlens_k=sk, alibi_slopes=sl, **mask)
+        runs.append((o, lse, *g))
+    torch.cuda.synchronize()
+    (o0, l0, dq0, dk0, dv0), (o1, l1, dq1, dk1, dv1) = runs
+    assert torch.equal(l1, l0)
+    exps = {"O": ec, "dQ": eb + ec + ed, "dK": ea + ec + ed, "dV": ed}
+    # An fp16 result in fp16's subnormal range (below 2^-14) is rounded on an
+    # absolute grid of 2^-24, which does not scale: there the scaled result
+    # may differ by one such step, times the power of two.
+    sub = 2.0 ** -24 if dtype == "f16" else 0.0
+    for name, a, b in (("O", o1, o0), ("dQ", dq1, dq0), ("dK", dk1, dk0), ("dV", dv1, dv0)):
+        s = 2.0 ** exps[name]
+        err = (a.double() - b.double() * s).abs()
+        lim = torch.where(b.double().abs() < 2.0 ** -14, sub * s, 0.0)
+        assert (err <= lim).all(), f"{name} is not the standard result times 2^{exps[name]}"
+    f64 = lambda t: t.double().cpu().numpy()
+    ref = attention_backward(*(f64(t) for t in big), seqlens_k=d["seqlens_k"].numpy(),
+                             alibi_slopes=None if sl is None else sl.cpu().numpy(), **mask)
+    # The normalised slices are larger than N(0, 1) draws, and so are the
+    # gradients: the bound adds the output's own rounding (2^-8 |ref|, as in
+    # the ALiBi cases).
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq1, dk1, dv1), ref):
+        s = 2.0 ** exps[name]
+        assert_close(got.cpu() / s, want / s, TOL["bf16"]["grad"], name, rel=BF16_HALF_ULP)
