@@ -95,9 +95,13 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(const void* p) {
 }
 
 // Four fp32 values -> four e4m3 bytes (round to nearest even), first value
-// in the lowest byte.
+// in the lowest byte. The two converts write the low and the high half of the
+// word, so its prior contents never matter; the builtin takes them as an
+// input, which costs a register clear per word, so the first convert is
+// written out with a plain output operand.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w;
+  asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(w) : "v"(a), "v"(b));
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -202,7 +206,6 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_wa
   for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16_t{};
   float m_ref = -1e30f, l_part = 0.f;
   f32x16_t sacc[2];
-  bool sact = false;
 
   // start(t): S^T = K(t) Q^T, masked on tiles that cross a mask edge. The
   // accumulator value i of block kb in lane (ln, hf) is the score of query
@@ -211,8 +214,6 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_wa
     constexpr int buf = decltype(bufc)::value;
     const char* sk = smem + (2 * buf) * C::TILE;
     const int kt = t * C::BN;
-    sact = kt < wkhi && kt + C::BN > wklo;
-    if (!sact) return;
     sacc[0] = f32x16_t{};
     sacc[1] = f32x16_t{};
 #pragma unroll
@@ -241,14 +242,12 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_wa
   auto finish = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const char* sv = smem + (2 * buf + 1) * C::TILE;
-    if (!sact) return;
     // Fast path without the tile max: P' = 2^(c2 S - M + 3) against the
     // current M; if a lane's sum exceeds 448 (so possibly one P' does), redo
     // the tile with M raised to the exact running max.
     float acc = 0.f;
     i32x8_t pb;
     auto exps = [&](float mu) __attribute__((always_inline)) {
-      acc = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -257,12 +256,13 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_wa
           const float p1 = exp2_fast(fmaf(sacc[kb][i + 1], p.scale_log2, -mu));
           const float p2 = exp2_fast(fmaf(sacc[kb][i + 2], p.scale_log2, -mu));
           const float p3 = exp2_fast(fmaf(sacc[kb][i + 3], p.scale_log2, -mu));
-          acc += (p0 + p1) + (p2 + p3);
+          const float g = (p0 + p1) + (p2 + p3);
+          acc = (kb == 0 && i == 0) ? g : acc + g;
           pb[4 * kb + (i >> 2)] = pack_fp8x4(p0, p1, p2, p3);
         }
     };
     exps(m_ref - 3.f);
-    if (__builtin_amdgcn_readfirstlane(__ballot(!(acc <= 448.f)) != 0)) {
+    if (__builtin_amdgcn_ballot_w64(!(acc <= 448.f)) != 0) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -293,8 +293,11 @@ __global__ void __launch_bounds__(Fp8Shape<D>::NW * 64) __attribute__((amdgpu_wa
   using B1 = std::integral_constant<int, 1>;
   auto interval = [&](int t, auto cur, auto nxt) __attribute__((always_inline)) {
     if (t + 1 < t1) issue_tile(t + 1, nxt);
-    start(t, cur);
-    finish(cur);
+    // Tiles that no query row of this wave sees are skipped whole.
+    if (t * C::BN < wkhi && t * C::BN + C::BN > wklo) {
+      start(t, cur);
+      finish(cur);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
