@@ -160,18 +160,14 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
   for (int qb = 0; qb < C::QB; ++qb) { m_ref[qb] = -INFINITY; l_part[qb] = 0.f; }
   bool m_finite = false;  // wave-uniform: every row of the wave has a finite M
 
-  // S^T of the tile a wave is working on, and whether it holds any key the
-  // wave's rows may see (wave-uniform).
+  // S^T of the tile a wave is working on.
   f32x16_t sacc[C::KB][C::QB];
-  bool sact = false;
 
   // start(t): S^T = K(t) Q^T on MFMA, masked on tiles that cross a mask edge.
   auto start = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const char* sk = smem + (2 * buf) * C::TILE;
     const int kt = t * C::BN;
-    sact = kt < wkhi && kt + C::BN > wklo;
-    if (!sact) return;
     // The 32-key blocks are independent accumulation chains whose MFMAs
     // alternate. The K operands are read PF d-steps ahead of their MFMAs; the
     // scheduling barriers keep the compiler from sinking the reads back to
@@ -236,7 +232,6 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
   auto finish = [&](auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const char* sv = smem + (2 * buf + 1) * C::TILE;
-    if (!sact) return;
     // P = 2^(c2 S - M) against the current reference M. Once a row has seen
     // a visible key, M never exceeds its true running max, so its sum l >= 1
     // and nothing underflows; the only hazard is a new score far above M.
@@ -251,14 +246,15 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
     auto exps = [&](const float (&m_use)[C::QB]) {
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
-        float acc = 0.f;
+        float acc;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
             const float p0 = exp2_fast(fmaf(sacc[kb][qb][i], p.scale_log2, -m_use[qb]));
             const float p1 = exp2_fast(fmaf(sacc[kb][qb][i + 1], p.scale_log2, -m_use[qb]));
-            acc += p0 + p1;  // fp32 sum of the unrounded P (LSE must hold to 1e-3 on short rows)
+            // fp32 sum of the unrounded P (LSE must hold to 1e-3 on short rows)
+            acc = (kb == 0 && i == 0) ? p0 + p1 : acc + (p0 + p1);
             pk[qb][2 * kb + (i >> 3)][(i & 7) >> 1] = E::pack2(p0, p1);
           }
         rsum[qb] = acc;
@@ -270,7 +266,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
       bool big = false;
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) big |= !(rsum[qb] <= kPmax);
-      slow = __builtin_amdgcn_readfirstlane(__ballot(big) != 0);
+      slow = __builtin_amdgcn_ballot_w64(big) != 0;
     }
     if (slow) {  // wave-uniform, rare: first visible tile, or a score far above M
       bool fin = true;
@@ -291,7 +287,7 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
         fin &= m_new != -INFINITY;
         m_use[qb] = (m_new == -INFINITY) ? 0.f : m_new;
       }
-      m_finite = __builtin_amdgcn_readfirstlane(__ballot(!fin) == 0);
+      m_finite = __builtin_amdgcn_ballot_w64(!fin) == 0;
       exps(m_use);
     }
 #pragma unroll
@@ -329,8 +325,11 @@ __global__ void __launch_bounds__(FwdCfg<D>::NW * 64) fwd_h16_kernel(FwdParams p
   // tile visible and release the buffer just read.
   auto interval = [&](int t, auto cur, auto nxt) {
     if (t + 1 < t1) issue_tile(t + 1, nxt);
-    start(t, cur);
-    finish(cur);
+    // Tiles that no query row of this wave sees are skipped whole.
+    if (t * C::BN < wkhi && t * C::BN + C::BN > wklo) {
+      start(t, cur);
+      finish(cur);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
