@@ -11,7 +11,7 @@
 // (The article's code sums P * dP over one key block only; the full-row sum
 // is what its own Jacobian gives, and is what is used here.)
 //
-// Four kernels, no atomics, so the result is deterministic (the flash_attn
+// Three kernels, no atomics, so the result is deterministic (the flash_attn
 // docstring's deterministic backward, claire-chang.com notes):
 //   bwd_prep_kernel : per row D_i (from O and dO) and LSE log2 e; fp16 copies
 //                     of Q, K and dO; per block the maxima of |Q|, |K|, |V|,
@@ -19,10 +19,12 @@
 //   bwd_rescale_kernel : rewrites the copies of a slice whose maxima leave
 //                     fp16's comfortable range (operand range, below);
 //                     returns at once for every other slice.
-//   bwd_dkdv_kernel : one work-group per key block; each wave keeps K, V, dK
+//   bwd_kvq_kernel  : the dK/dV work-groups, then the dQ work-groups, in one
+//                     grid (the two passes are independent):
+//     dK/dV block   : one work-group per key block; each wave keeps K, V, dK
 //                     and dV of 32 keys in registers and streams the query
 //                     tiles (Q, dO and the row statistics) through LDS.
-//   bwd_dq_kernel   : one work-group per query block; each wave keeps Q, dO
+//     dQ block      : one work-group per query block; each wave keeps Q, dO
 //                     and dQ of 32 queries in registers and streams the key
 //                     tiles (K, V) through LDS.
 // Every product with P or dS as an operand runs on fp16 MFMA: P and dS carry
@@ -219,16 +221,15 @@ struct KvCfg {
 // Query rows at or past N arrive as zeros (Q, dO and both statistics), which
 // makes every term they add zero.
 template <int D, bool ALIBI, typename T>
-__global__ void __launch_bounds__(KvCfg<D>::NW * 64) bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_block(const BwdParams& p, int nblk, int wg, char* smem) {
   using E = Elt16<T>;
   using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hf = lane >> 5;
   int bh, kblk;
-  map_block(p.B * p.H, p.nblk, p.xcd_groups, 0, bh, kblk);
+  map_index(wg, p.B * p.H, nblk, p.xcd_groups, 0, bh, kblk);
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
@@ -500,17 +501,16 @@ struct KvPairCfg {
 // so a tile's statistics sit in LDS split by kind: one 16-byte read brings
 // four rows' worth of the one a wave uses.
 template <int D, bool ALIBI, typename T>
-__global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_pair_block(const BwdParams& p, int nblk, int wg, char* smem) {
   using E = Elt16<T>;
   using C = KvPairCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF + C::NP * C::XCH];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave % C::NP, role = wave / C::NP;
   const int ln = lane & 31, hf = lane >> 5;
   int bh, kblk;
-  map_block(p.B * p.H, p.nblk, p.xcd_groups, 0, bh, kblk);
+  map_index(wg, p.B * p.H, nblk, p.xcd_groups, 0, bh, kblk);
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
@@ -620,14 +620,15 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
     f32x16_t pa[C::QS];   // role 1: dP
     if (active) {
       if (role == 0) {
-        f32x16_t sall[C::QS];  // the sub-blocks' chains alternate (slack for each operand read)
-#pragma unroll
-        for (int qs = 0; qs < C::QS; ++qs) sall[qs] = f32x16_t{};
+        // The sub-blocks' chains alternate (slack for each operand read); the
+        // first step takes a zero accumulator as its constant operand.
+        f32x16_t sall[C::QS];
 #pragma unroll
         for (int s = 0; s < C::DS; ++s)
 #pragma unroll
           for (int qs = 0; qs < C::QS; ++qs)
-            sall[qs] = mfma_f16(*(const f16x8_t*)(sq + qs * 32 * C::CPR * 16 + roff[s]), kv[s], sall[qs]);
+            sall[qs] = mfma_f16(*(const f16x8_t*)(sq + qs * 32 * C::CPR * 16 + roff[s]), kv[s],
+                                s == 0 ? f32x16_t{} : sall[qs]);
 #pragma unroll
         for (int qs = 0; qs < C::QS; ++qs) {
           f32x16_t sa = sall[qs];
@@ -658,12 +659,11 @@ __global__ void __launch_bounds__(KvPairCfg<D>::NW * 64) bwd_dkdv_pair_kernel(Bw
         for (int ks = 0; ks < C::KS; ++ks) *(u32x4_t*)(xch + (ks * 64 + lane) * 16) = pk[ks];
       } else {
 #pragma unroll
-        for (int qs = 0; qs < C::QS; ++qs) pa[qs] = f32x16_t{};
-#pragma unroll
         for (int s = 0; s < C::DS; ++s)
 #pragma unroll
           for (int qs = 0; qs < C::QS; ++qs)
-            pa[qs] = mfma_f16(*(const f16x8_t*)(so + qs * 32 * C::CPR * 16 + roff[s]), kv[s], pa[qs]);
+            pa[qs] = mfma_f16(*(const f16x8_t*)(so + qs * 32 * C::CPR * 16 + roff[s]), kv[s],
+                              s == 0 ? f32x16_t{} : pa[qs]);
       }
     }
     __syncthreads();  // P of every pair is in LDS
@@ -793,17 +793,16 @@ struct DqCfg {
 //                                       to fp16 from the accumulators).
 // K comes from the fp16 copy (its products meet dS), V stays bf16.
 template <int D, bool ALIBI, typename T>
-__global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_block(const BwdParams& p, int nblk, int wg, char* smem) {
   using E = Elt16<T>;
   using vec8 = typename E::vec8;
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE];  // [buf][K | V]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hf = lane >> 5;
   int bh, qblk;
-  map_block(p.B * p.H, p.nblk, p.xcd_groups, p.mask.wr >= 0, bh, qblk);
+  map_index(wg, p.B * p.H, nblk, p.xcd_groups, p.mask.wr >= 0, bh, qblk);
   const int b = bh / p.H, h = bh - b * p.H;
   const int N = p.N;
   const int kl = key_len(p.mask, b, N);
@@ -971,6 +970,38 @@ __global__ void __launch_bounds__(DqCfg<D>::NW * 64) bwd_dq_kernel(BwdParams p) 
   }
 }
 
+// ---------------------------------------------------------------- kernels
+
+// dK/dV and dQ in one grid: the B H nblk_kv dK/dV work-groups first, then the
+// B H nblk_q dQ work-groups. The two passes read the same pre-pass outputs and
+// write disjoint gradients, so nothing orders them; in one grid the dQ groups
+// (longest first under a causal mask) start as soon as dK/dV groups retire,
+// which fills the tail that a causal mask leaves in each pass on its own
+// (one launch instead of two). The groups of both kinds have the same size;
+// LDS is the larger of the two layouts.
+template <int D>
+struct KvqShape {
+  static constexpr int NW = D == 128 ? KvPairCfg<D>::NW : KvCfg<D>::NW;
+  static constexpr int KV_LDS = D == 128 ? 2 * KvPairCfg<D>::BUF + KvPairCfg<D>::NP * KvPairCfg<D>::XCH
+                                         : 2 * KvCfg<D>::BUF;
+  static constexpr int Q_LDS = 2 * 2 * DqCfg<D>::TILE;
+  static constexpr int LDS = KV_LDS > Q_LDS ? KV_LDS : Q_LDS;
+  static_assert(NW == DqCfg<D>::NW, "dK/dV and dQ work-groups must have the same size");
+};
+
+template <int D, bool ALIBI, typename T>
+__global__ void __launch_bounds__(KvqShape<D>::NW * 64) bwd_kvq_kernel(BwdParams p, int nblk_kv, int nblk_q) {
+  __shared__ __attribute__((aligned(1024))) char smem[KvqShape<D>::LDS];
+  const int nkv = p.B * p.H * nblk_kv;
+  const int i = blockIdx.x;
+  if (i < nkv) {
+    if constexpr (D == 128) dkdv_pair_block<D, ALIBI, T>(p, nblk_kv, i, smem);
+    else dkdv_block<D, ALIBI, T>(p, nblk_kv, i, smem);
+  } else {
+    dq_block<D, ALIBI, T>(p, nblk_q, i - nkv, smem);
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 
 template <int D, bool ALIBI, typename T>
@@ -985,21 +1016,14 @@ static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_prep_kernel<D, T>), pgrid, dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_rescale_kernel<D, T>), dim3((unsigned)((long long)p.B * p.H * kRescaleGroups)),
                      dim3(256), 0, stream, p);
-  // Measured on MI355X: the one-wave form is faster at headdim 64 (two
+  // Measured on MI355X: the one-wave dK/dV form is faster at headdim 64 (two
   // waves per SIMD either way, half the barriers); at headdim 128 only the
   // pair form keeps its state in VGPRs.
-  if constexpr (D == 128) {
-    p.nblk = (p.N + KvPairCfg<D>::BK - 1) / KvPairCfg<D>::BK;
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, ALIBI, T>), dim3(p.B * p.H * p.nblk),
-                       dim3(KvPairCfg<D>::NW * 64), 0, stream, p);
-  } else {
-    p.nblk = (p.N + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI, T>), dim3(p.B * p.H * p.nblk),
-                       dim3(KvCfg<D>::NW * 64), 0, stream, p);
-  }
-  p.nblk = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI, T>), dim3(p.B * p.H * p.nblk), dim3(DqCfg<D>::NW * 64),
-                     0, stream, p);
+  const int nblk_kv = (p.N + (D == 128 ? KvPairCfg<D>::BK : KvCfg<D>::BK) - 1) /
+                      (D == 128 ? KvPairCfg<D>::BK : KvCfg<D>::BK);
+  const int nblk_q = (p.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+  hipLaunchKernelGGL((bwd_kvq_kernel<D, ALIBI, T>), dim3((unsigned)((long long)p.B * p.H * (nblk_kv + nblk_q))),
+                     dim3(KvqShape<D>::NW * 64), 0, stream, p, nblk_kv, nblk_q);
   return hipGetLastError();
 }
 

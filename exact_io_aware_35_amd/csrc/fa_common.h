@@ -60,9 +60,11 @@ __device__ __forceinline__ bool visible(const MaskParams& m, int kl, int i, int 
 // stay in one L2; within an XCD the blocks are interleaved over its heads and,
 // for longest-first, ordered by decreasing block index (more keys under a
 // causal mask).
-__device__ __forceinline__ void map_block(int nbh, int nblk, int xcd_groups, int longest_first,
+// map_index takes the id explicitly (a kernel that runs two kinds of
+// work-group in one grid passes each kind's own index; the XCD of index i is
+// still i % 8 as long as the first kind's count divides by 8).
+__device__ __forceinline__ void map_index(int i, int nbh, int nblk, int xcd_groups, int longest_first,
                                           int& bh, int& blk) {
-  const int i = blockIdx.x;
   int rank;
   if (xcd_groups > 0) {
     const int hpx = nbh / 8;           // (b, h) per XCD
@@ -74,6 +76,10 @@ __device__ __forceinline__ void map_block(int nbh, int nblk, int xcd_groups, int
     rank = i / nbh;
   }
   blk = longest_first ? (nblk - 1 - rank) : rank;
+}
+__device__ __forceinline__ void map_block(int nbh, int nblk, int xcd_groups, int longest_first,
+                                          int& bh, int& blk) {
+  map_index(blockIdx.x, nbh, nblk, xcd_groups, longest_first, bh, blk);
 }
 
 // ALiBi slope of (b, h) in raw score units: the bias -slope |i - j| is added

@@ -69,7 +69,6 @@ struct BwdParams {
   int rs_q;              // elements between sequence positions of Q, K and V
   int rs_o;              // ... of O and dO
   int rs_g;              // ... of dQ, dK and dV (the fp16 copies use H * D)
-  int nblk;              // blocks per (b, h) along the dimension a kernel tiles
   float scale;           // softmax_scale
   float scale_log2;      // softmax_scale * log2(e)
   int xcd_groups;
