@@ -7,6 +7,9 @@ on stdout is one JSON object: TFLOP/s with FLOPs = 4 B H N^2 D (halved for a
 causal mask), the roofline of the forward kernel measured with HIP events on
 the stream it runs on, the fp64 CPU oracle timed on a bounded sample, and the
 same shape's backward (timed separately, FLOPs counted as 2.5x the forward's).
+Before the W warm-up launches the forward runs back to back for 2 s while the
+shader clock is sampled (the line's "clock" object), so the warm-up and the K
+timed launches run at the clock this load holds, not inside its ramp.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --extra      # also write fwd/bwd lines for every workload
@@ -99,14 +102,17 @@ MI355X_CUS = 256
 BF16_FLOP_PER_CLK_PER_CU = 4096   # dense 32x32x16 bf16 MFMA rate: 2.5 PF/s at 2.4 GHz
 
 
-def sample_gfx_clock(fn, seconds=0.6, period_s=0.004):
+def sample_gfx_clock(fn, seconds=2.0, period_s=0.004):
     """Shader clock while fn() runs back to back for about `seconds`.
 
     The GPU's own telemetry is read through amdsmi from a host thread while
     the launches run: the gpu_metrics table's per-XCD current graphics clocks
-    (falling back to the driver's current GFX clock). Returns a dict with the
-    median over the samples and how it was read, or None with a reason if the
-    telemetry is not readable here."""
+    (falling back to the driver's current GFX clock). The table changes only
+    a few times a second and lags the clock: after an idle spell its first
+    values are the idle clock and then points of the ramp. The value read
+    last, after `seconds` of back-to-back launches, is the one reported;
+    every change of value is listed with the time it was first read. Returns
+    None with a reason if the telemetry is not readable here."""
     import threading
     import torch
     try:
@@ -134,7 +140,7 @@ def sample_gfx_clock(fn, seconds=0.6, period_s=0.004):
         while not stop.is_set():
             try:
                 v, src[0] = read()
-                samples.append(v)
+                samples.append((time.perf_counter() - t0, v))
             except Exception:  # noqa: BLE001
                 pass
             stop.wait(period_s)
@@ -142,9 +148,9 @@ def sample_gfx_clock(fn, seconds=0.6, period_s=0.004):
     for _ in range(50):  # clock up before sampling starts
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     th = threading.Thread(target=poll, daemon=True)
     th.start()
-    t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(50):
             fn()
@@ -157,11 +163,12 @@ def sample_gfx_clock(fn, seconds=0.6, period_s=0.004):
         pass
     if not samples:
         return {"mhz": None, "why": "no telemetry sample could be read"}
-    samples.sort()
-    return {"mhz": samples[len(samples) // 2], "samples": len(samples),
-            "min_mhz": samples[0], "max_mhz": samples[-1], "source": src[0],
-            "how": f"sampled every {period_s * 1e3:.0f} ms from a host thread while the "
-                   f"forward ran back to back for {seconds:.1f} s"}
+    changes = [[round(t, 3), v] for i, (t, v) in enumerate(samples)
+               if i == 0 or v != samples[i - 1][1]]
+    return {"mhz": samples[-1][1], "samples": len(samples),
+            "changes_s_mhz": changes[-8:], "source": src[0],
+            "how": f"read every {period_s * 1e3:.0f} ms from a host thread while the "
+                   f"forward ran back to back for {seconds:.1f} s; the last value read"}
 
 
 def load_traffic():
@@ -448,9 +455,11 @@ def oracle_rates(w, seconds):
     return out
 
 
-def run_workload(w, steps, warmup, backward=False, variant=None):
+def run_workload(w, steps, warmup, backward=False, variant=None, before=None):
     """(fwd ms, bwd ms or None) for workload w on cuda:0. variant: None, "alibi"
-    (the usual geometric slopes per head) or "qkvpacked" (one packed input)."""
+    (the usual geometric slopes per head) or "qkvpacked" (one packed input).
+    before(fwd), if given, runs once the forward is built and before its
+    warm-up launches."""
     import torch
     import exact_io_aware_35_amd as fa
     from exact_io_aware_35_amd.inputs import make_inputs
@@ -464,6 +473,8 @@ def run_workload(w, steps, warmup, backward=False, variant=None):
     if w.dtype == "fp8":
         ds = d["descale"]
         fwd = fa.prepare_forward_fp8(q, k, v, out, lse, ds["q"], ds["k"], ds["v"], **kw)
+        if before is not None:
+            before(fwd)
         return time_gpu(fwd, steps, warmup), None, (fwd, q)
     if variant is None:
         fwd = fa.prepare_forward(q, k, v, out, lse, **kw)
@@ -474,6 +485,8 @@ def run_workload(w, steps, warmup, backward=False, variant=None):
     else:
         qkv = torch.stack([q, k, v], dim=2).contiguous()
         fwd = lambda: fa.forward_qkvpacked(qkv, out=out, lse=lse, **kw)
+    if before is not None:
+        before(fwd)
     t_f = time_gpu(fwd, steps, warmup)
     t_b = None
     if backward:
@@ -496,13 +509,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed launches first; the GPU clock takes ~400 back-to-back "
-                         "launches of the metric forward (~50 ms) to reach its steady state")
+                    help="untimed launches before the timed ones (after the clock sampling, "
+                         "which already runs the forward back to back for 2 s)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip sampling the shader clock (amdsmi) after the timed region")
+                    help="skip sampling the shader clock (amdsmi) before the warm-up")
     ap.add_argument("--extra", action="store_true",
                     help="also time fwd/bwd of every workload; lines go to stderr")
     ap.add_argument("--oracle-all", type=float, default=None, metavar="SECONDS",
@@ -557,9 +570,16 @@ def main():
     print(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}",
           file=sys.stderr, flush=True)
 
+    # The shader clock is sampled first, while the forward runs back to back
+    # for 2 s: it reports the clock this load holds, and the warm-up and
+    # timed launches that follow then run at that steady state instead of
+    # inside the clock's ramp after an idle spell (about 400 launches, which
+    # a short warm-up does not cover).
+    clock = {}
+    before = None if args.no_clock else (lambda fn: clock.update(sample_gfx_clock(fn)))
     # The backward is built for the 16-bit types.
     ms, bwd_ms, (fwd, q) = run_workload(w, args.steps, args.warmup,
-                                        backward=w.dtype in ("bf16", "f16"))
+                                        backward=w.dtype in ("bf16", "f16"), before=before)
     med_ms, mean_ms, min_ms = per_launch_ms(fwd, min(args.steps, 100))
     flops = fwd_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -605,13 +625,15 @@ def main():
             "frac_of_mfma_peak": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),
             "flops": 2.5 * flops},
     }
-    if not args.no_clock and w.dtype in ("bf16", "f16"):
-        clk = sample_gfx_clock(fwd)
-        if clk.get("mhz"):
-            peak_clk = MI355X_CUS * BF16_FLOP_PER_CLK_PER_CU * clk["mhz"] * 1e6 / 1e12
-            clk["peak_tflops_at_clock"] = round(peak_clk, 1)
-            clk["frac_at_clock"] = round(kernel_tflops / peak_clk, 4)
-        line["clock"] = clk
+    if clock:
+        if clock.get("mhz"):
+            # The dtype's dense peak scales with the clock (bf16: 4096 FLOP per
+            # clock per CU; the other dtypes in proportion to their peaks).
+            peak_clk = (MI355X_CUS * BF16_FLOP_PER_CLK_PER_CU * clock["mhz"] * 1e6 / 1e12
+                        * peak / PEAK_TFLOPS["bf16"])
+            clock["peak_tflops_at_clock"] = round(peak_clk, 1)
+            clock["frac_at_clock"] = round(kernel_tflops / peak_clk, 4)
+        line["clock"] = clock
     if args.extra:
         for name, wk in WORKLOADS.items():
             tf, tb, _ = run_workload(wk, 20, 3, backward=wk.backward or name == METRIC_WORKLOAD)
