@@ -307,17 +307,24 @@ def pmc_summary(dirs, workload):
     directory per pass of PMC_PASSES -> profiles/pmc_<workload>.txt."""
     import csv
     import glob
-    vals = {}
+    vals, durs = {}, {}
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if "fa::" not in r["Kernel_Name"] and not r["Kernel_Name"].startswith("_ZN2fa"):
                     continue
-                vals.setdefault(pretty_kernel(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                name = pretty_kernel(r["Kernel_Name"])
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    durs.setdefault(name, []).append(
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     with open(os.path.join(ROOT, "profiles", f"pmc_{workload}.txt"), "w") as f:
         f.write(f"rocprofv3 counter summary of bench.py on {workload}: per kernel, the mean of "
-                "each counter over its dispatches (one dispatch's total).\n")
+                "each counter over its dispatches (one dispatch's total). For dispatches of "
+                "100 us or more, the clock they ran at (GRBM_GUI_ACTIVE / 8 XCDs over the "
+                "dispatch's timestamps) and the MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES "
+                "over 1024 SIMDs x those cycles).\n")
         for i, c in enumerate(PMC_PASSES):
             f.write(f"pass {i + 1}: " + PMC_CMD.format(counters=c, workload=workload) + "\n")
         for name, cs in vals.items():
@@ -333,6 +340,23 @@ def pmc_summary(dirs, workload):
                         f"{m['SQ_INSTS_VALU_TRANS_F32'] / m['SQ_INSTS_MFMA']:.2f} transcendental, "
                         f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} LDS instructions; "
                         f"LDS bank conflicts {m['SQ_LDS_BANK_CONFLICT']:.0f}\n")
+            except (KeyError, ZeroDivisionError):
+                pass
+            try:
+                # GRBM_GUI_ACTIVE counts the cycles of each of the 8 XCDs, summed;
+                # SQ_VALU_MFMA_BUSY_CYCLES sums every MFMA's cycles over the 1024
+                # SIMDs (it equals the MFMA count x 32 for 32x32x16 bf16). The
+                # GRBM count also takes in cycles outside the dispatch's own
+                # timestamps, a few microseconds' worth, so the two ratios are
+                # written only for dispatches of 100 us or more.
+                cyc = m["GRBM_GUI_ACTIVE"] / 8
+                ns = sum(durs[name]) / len(durs[name])
+                if ns < 100e3 or not m.get("SQ_INSTS_MFMA"):
+                    raise KeyError(name)
+                f.write(f"  -> clock {cyc / ns:.2f} GHz (GRBM_GUI_ACTIVE / 8 over the dispatch's "
+                        f"{ns / 1e3:.1f} us); MFMA busy "
+                        f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 4 * MI355X_CUS):.3f} of the "
+                        f"SIMD-cycles\n")
             except (KeyError, ZeroDivisionError):
                 pass
 
