@@ -302,9 +302,9 @@ PMC_CMD = ("rocprofv3 --pmc {counters} --output-format csv -- python bench.py --
            "{workload} --steps 5 --warmup 1 --no-cpu-baseline --no-clock")
 
 
-def pmc_summary(dirs, workload):
+def pmc_summary(dirs, workload, out_dir=None):
     """Per-kernel counter means (one dispatch) from one rocprofv3 --pmc output
-    directory per pass of PMC_PASSES -> profiles/pmc_<workload>.txt."""
+    directory per pass of PMC_PASSES -> <out_dir or profiles>/pmc_<workload>.txt."""
     import csv
     import glob
     vals, durs = {}, {}
@@ -319,7 +319,7 @@ def pmc_summary(dirs, workload):
                 if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                     durs.setdefault(name, []).append(
                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    with open(os.path.join(ROOT, "profiles", f"pmc_{workload}.txt"), "w") as f:
+    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"pmc_{workload}.txt"), "w") as f:
         f.write(f"rocprofv3 counter summary of bench.py on {workload}: per kernel, the mean of "
                 "each counter over its dispatches (one dispatch's total). For dispatches of "
                 "100 us or more, the clock they ran at (GRBM_GUI_ACTIVE / 8 XCDs over the "
