@@ -1,7 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
 include/fa.h declares, and rejects bad arguments before any launch."""
 
-import ctypes
 import os
 import re
 
