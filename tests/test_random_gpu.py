@@ -46,7 +46,7 @@ def close(got, want, hu, what, tol=2e-2):
     got = got.float().numpy().astype(np.float64)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     excess = (np.abs(got - want) - hu * np.abs(want)).max()
-    assert excess <= tol, f"{what}: error exceeds {tol} + {hu} |ref| by {excess:.3g}"
+    assert excess <= tol, f"{what}: max of |err| - {hu} |ref| is {excess:.3g} > {tol}"
 
 
 @pytest.mark.parametrize("seed", range(100))
